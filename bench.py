@@ -1,0 +1,256 @@
+"""Benchmark of the blockwise exact-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extras] [--no-cpu]
+
+Workload: causal multi-head attention, n=2, l=2048, h=h_kv=16, d=128, bf16,
+scale 1/sqrt(128), synthetic N(0,1) inputs resident in HBM.  A step is one
+attn_fwd call over that batch (through the C ABI).  Prints one JSON line:
+forward TFLOP/s (algorithmic FLOPs: 4*d per allowed query/key pair per head),
+the roofline of the forward kernel, and the fp64 CPU oracle's rate on a
+bounded sample of the same workload.  --extras adds the other workloads
+(ring share with its merges, sliding window, long-context forward and
+backward) as separately timed figures.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, torch):
+    """Median/mean per-call time (ms) of fn() with events on the current
+    stream (the one every library call is launched on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(np.median(ts)), float(np.mean(ts))
+
+
+def cpu_baseline(x, w, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    whole heads of the same inputs, as many as fit in about `seconds`."""
+    import oracle
+    from blockwise_exact_attention_amd.flops import allowed_pairs, fwd_flops
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    pairs = allowed_pairs(w.l_q, w.l_k, True)
+    heads_all = [(b, hq) for b in range(w.n) for hq in range(w.h)]
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(heads_all) and time.perf_counter() - t0 < seconds:
+        oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale, True,
+                             heads=[heads_all[done]])
+        done += 1
+    dt = time.perf_counter() - t0
+    flops = fwd_flops(1, done, w.d, pairs)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads_all)} (batch, head) pairs of the "
+                      f"same workload, fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); a "
+              "multi-GPU run of this path is not part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from blockwise_exact_attention_amd import attention as A
+    from blockwise_exact_attention_amd.flops import (allowed_pairs, fwd_flops,
+                                                     fwd_bytes, bwd_flops,
+                                                     merge_bytes)
+    from blockwise_exact_attention_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS["C2"]
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(x[s]).to(torch.bfloat16).to(dev)
+                  for s in ("q", "k", "v"))
+    out = torch.empty_like(tq)
+    lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
+    pairs = allowed_pairs(w.l_q, w.l_k, True)
+    flops = fwd_flops(w.n, w.h, w.d, pairs)
+
+    def step():
+        A.attn_fwd(tq, tk, tv, out, lse, w.softmax_scale, True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch durations on the launch stream, over the timed region
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = float(per.mean())
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+
+    rec = {
+        "metric": "attention fwd TFLOP/s (causal bf16, d=128) and % of MFMA bf16 peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": w.n, "l": w.l_q, "h": w.h,
+                   "h_kv": w.h_kv, "d": w.d, "causal": True,
+                   "allowed_pairs_per_head": pairs,
+                   "algorithmic_gflop": round(flops / 1e9, 3)},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "fwd_bf16_kernel<128,64>",
+                     "kernel_ms_mean": round(kern_ms, 5),
+                     "kernel_ms_median": round(float(np.median(per)), 5),
+                     "algorithmic_bytes": fwd_bytes(w.n, w.l_q, w.l_k, w.h,
+                                                    w.h_kv, w.d, 2)},
+    }
+
+    if args.extras:
+        rec["extras"] = extras(A, torch, args, allowed_pairs, fwd_flops,
+                               bwd_flops, merge_bytes, WORKLOADS, make_inputs)
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
+           WORKLOADS, make_inputs):
+    dev = torch.device("cuda:0")
+    res = {}
+    steps = max(10, args.steps // 4)
+
+    def t(xs):
+        return torch.from_numpy(xs).to(torch.bfloat16).to(dev)
+
+    # ring share, rank 7 of 8, GQA 32/8
+    w = WORKLOADS["C3"]
+    x = make_inputs(w)
+    tq = t(x["q"])
+    kc = [t(c) for c in x["k_chunks"]]
+    vc = [t(c) for c in x["v_chunks"]]
+    share = A.RingShare(tq, w.softmax_scale, True, x["q_offset"])
+    fwd_ms = []
+    merge_ms = []
+    for s in range(8):
+        def f(s=s):
+            A.attn_fwd(tq, kc[s], vc[s], share.blk, share.lse_blk,
+                       w.softmax_scale, True, -1, -1, x["q_offset"],
+                       x["k_offsets"][s])
+        fwd_ms.append(timed(f, steps, 5, torch)[0])
+    A.attn_acc_init(share.acc, share.lse_acc)
+    merge_ms.append(timed(lambda: A.attn_merge(share.acc, share.lse_acc,
+                                               share.blk, share.lse_blk),
+                          steps, 5, torch)[0])
+    e2e = timed(lambda: share.run(kc, vc, x["k_offsets"]), steps, 3, torch)[0]
+    pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, 7168, 1024 * s)
+                for s in range(8))
+    fl = fwd_flops(1, 32, 128, pairs)
+    mb = merge_bytes(1, 1024, 32, 128, 2)
+    res["ring_share_rank7"] = {
+        "fwd_tflops_sum_of_8": round(fl / (sum(fwd_ms) * 1e-3) / 1e12, 2),
+        "fwd_ms_per_step": [round(v, 4) for v in fwd_ms],
+        "merge_ms": round(merge_ms[0], 4),
+        "merge_gbs_warm": round(mb / (merge_ms[0] * 1e-3) / 1e9, 1),
+        "end_to_end_ms": round(e2e, 4)}
+    del share, kc, vc, tq
+
+    # sliding window
+    w = WORKLOADS["C4"]
+    x = make_inputs(w)
+    tq, tk, tv = t(x["q"]), t(x["k"]), t(x["v"])
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
+    ms = timed(lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True,
+                                  w.win_l, w.win_r), steps, 5, torch)[0]
+    pairs = allowed_pairs(w.l_q, w.l_k, True, w.win_l, w.win_r)
+    fl = fwd_flops(w.n, w.h, w.d, pairs)
+    res["window_256"] = {"ms": round(ms, 4),
+                         "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+    del tq, tk, tv, o, lse
+
+    # long context fwd (+ bwd)
+    w = WORKLOADS["C5"]
+    x = make_inputs(w)
+    tq, tk, tv, tdo = t(x["q"]), t(x["k"]), t(x["v"]), t(x["do"])
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
+    ms = timed(lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True),
+               max(5, steps // 4), 3, torch)[0]
+    pairs = allowed_pairs(w.l_q, w.l_k, True)
+    res["long_16k"] = {"fwd_ms": round(ms, 4),
+                       "fwd_tflops": round(fwd_flops(w.n, w.h, w.d, pairs)
+                                           / (ms * 1e-3) / 1e12, 2)}
+    try:
+        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        ws = torch.empty(A.bwd_workspace_bytes(w.n, w.l_q, w.l_k, w.h, w.h_kv,
+                                               w.d), dtype=torch.uint8,
+                         device=dev)
+        msb = timed(lambda: A.attn_bwd(tdo, tq, tk, tv, o, lse, dq, dk, dv,
+                                       w.softmax_scale, True, workspace=ws),
+                    max(5, steps // 8), 2, torch)[0]
+        res["long_16k"]["bwd_ms"] = round(msb, 4)
+        res["long_16k"]["bwd_tflops"] = round(
+            bwd_flops(w.n, w.h, w.d, pairs) / (msb * 1e-3) / 1e12, 2)
+    except Exception as e:  # the backward is reported when it runs
+        res["long_16k"]["bwd_error"] = str(e)
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,19 @@
+"""MI355X (gfx950) blockwise exact attention.
+
+The compute lives in libattn.so (hand-written HIP kernels behind the C ABI of
+include/attn.h).  `attention` is the torch binding; `inputs` and `workloads`
+describe the seeded synthetic inputs; `flops` the algorithmic work.
+"""
+from .attention import (  # noqa: F401
+    attn_fwd,
+    attn_merge,
+    attn_acc_init,
+    attn_acc_cast,
+    attn_bwd,
+    attention_forward,
+    attention_backward,
+    bwd_workspace_bytes,
+    ring_share,
+    RingShare,
+)
+from ._lib import AttnError, lib  # noqa: F401

@@ -1,0 +1,191 @@
+"""Python binding of the attention library: marshals torch tensors (device
+memory and the current stream) into the C ABI of include/attn.h.  Every step
+of the computation runs in the library's HIP kernels; this module only checks
+tensor metadata, allocates outputs when asked to, and forwards pointers.
+
+Layouts: q, out [n, l_q, h, d]; k, v [n, l_k, h_kv, d]; lse [n, h, l_q]
+float32.  Masking: absolute positions q_offset + i and k_offset + j, causal
+kpos <= qpos, inclusive window (win_l, win_r) with -1 for an open side.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import ATTN_BF16, ATTN_F32, check
+
+_DT = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype_code(t):
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def attn_fwd(q, k, v, out, lse, scale, causal=False, win_l=-1, win_r=-1,
+             q_offset=0, k_offset=0, stream=None):
+    """Forward into caller-provided `out` (q's dtype) and `lse` (float32)."""
+    _dev(q, k, v, out, lse)
+    n, l_q, h, d = q.shape
+    _, l_k, h_kv, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != n or k.shape[3] != d:
+        raise ValueError("k and v must be [n, l_k, h_kv, d] matching q")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(lse.shape) != (n, h, l_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [n, h, l_q]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    st = _lib.lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             out.data_ptr(), lse.data_ptr(), n, l_q, l_k, h,
+                             h_kv, d, float(scale), int(bool(causal)),
+                             int(win_l), int(win_r), int(q_offset),
+                             int(k_offset), _stream(stream), _dtype_code(q))
+    check("attn_fwd", st)
+    return out, lse
+
+
+def attention_forward(q, k, v, scale=None, causal=False, window=(-1, -1),
+                      q_offset=0, k_offset=0, stream=None):
+    """Allocate (O, LSE) and run the forward; scale defaults to 1/sqrt(d)."""
+    n, l_q, h, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    lse = torch.empty((n, h, l_q), dtype=torch.float32, device=q.device)
+    return attn_fwd(q, k, v, out, lse, scale, causal, window[0], window[1],
+                    q_offset, k_offset, stream)
+
+
+def attn_merge(out_acc, lse_acc, out_blk, lse_blk, stream=None):
+    """In-place merge of (out_blk, lse_blk) into the float32 accumulator."""
+    _dev(out_acc, lse_acc, out_blk, lse_blk)
+    n, l, h, d = out_acc.shape
+    if out_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32 \
+            or lse_blk.dtype != torch.float32:
+        raise ValueError("accumulator and LSEs must be float32")
+    if out_blk.shape != out_acc.shape or tuple(lse_acc.shape) != (n, h, l) \
+            or lse_blk.shape != lse_acc.shape:
+        raise ValueError("shape mismatch")
+    st = _lib.lib().attn_merge(out_acc.data_ptr(), lse_acc.data_ptr(),
+                               out_blk.data_ptr(), lse_blk.data_ptr(), n, l, h,
+                               d, _dtype_code(out_blk), _stream(stream))
+    check("attn_merge", st)
+    return out_acc, lse_acc
+
+
+def attn_acc_init(out_acc, lse_acc, stream=None):
+    _dev(out_acc, lse_acc)
+    n, l, h, d = out_acc.shape
+    if tuple(lse_acc.shape) != (n, h, l):
+        raise ValueError("shape mismatch")
+    st = _lib.lib().attn_acc_init(out_acc.data_ptr(), lse_acc.data_ptr(), n, l,
+                                  h, d, _stream(stream))
+    check("attn_acc_init", st)
+    return out_acc, lse_acc
+
+
+def attn_acc_cast(out_acc, out, stream=None):
+    _dev(out_acc, out)
+    n, l, h, d = out_acc.shape
+    if out.shape != out_acc.shape:
+        raise ValueError("shape mismatch")
+    st = _lib.lib().attn_acc_cast(out_acc.data_ptr(), out.data_ptr(), n, l, h,
+                                  d, _dtype_code(out), _stream(stream))
+    check("attn_acc_cast", st)
+    return out
+
+
+def bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d):
+    return int(_lib.lib().attn_bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d))
+
+
+def attn_bwd(dout, q, k, v, out, lse, dq, dk, dv, scale, causal=False,
+             win_l=-1, win_r=-1, q_offset=0, k_offset=0, workspace=None,
+             stream=None):
+    """Backward into caller-provided dq, dk, dv; `workspace` is a uint8 device
+    tensor of at least bwd_workspace_bytes(...) bytes (allocated if None)."""
+    _dev(dout, q, k, v, out, lse, dq, dk, dv)
+    n, l_q, h, d = q.shape
+    _, l_k, h_kv, _ = k.shape
+    need = bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace)
+    st = _lib.lib().attn_bwd(dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                             v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), n,
+                             l_q, l_k, h, h_kv, d, float(scale),
+                             int(bool(causal)), int(win_l), int(win_r),
+                             int(q_offset), int(k_offset), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(),
+                             _stream(stream), _dtype_code(q))
+    check("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attention_backward(dout, q, k, v, out, lse, scale=None, causal=False,
+                       window=(-1, -1), q_offset=0, k_offset=0, stream=None):
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    return attn_bwd(dout, q, k, v, out, lse, dq, dk, dv, scale, causal,
+                    window[0], window[1], q_offset, k_offset, None, stream)
+
+
+class RingShare:
+    """One device's share of ring attention, with its buffers allocated once:
+    the float32 accumulator (O, LSE), one block (O, LSE) per step and the
+    final output.  `run` launches acc_init, then attn_fwd + attn_merge per
+    key/value chunk with that chunk's absolute offset, then the final cast -
+    all on one stream, nothing synchronised (flash_sharding.py, ring_fwd)."""
+
+    def __init__(self, q, scale, causal, q_offset):
+        n, l, h, d = q.shape
+        self.q = q
+        self.scale = scale
+        self.causal = causal
+        self.q_offset = q_offset
+        dev = q.device
+        self.acc = torch.empty((n, l, h, d), dtype=torch.float32, device=dev)
+        self.lse_acc = torch.empty((n, h, l), dtype=torch.float32, device=dev)
+        self.blk = torch.empty_like(q)
+        self.lse_blk = torch.empty((n, h, l), dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(q)
+
+    def run(self, k_chunks, v_chunks, k_offsets, stream=None):
+        attn_acc_init(self.acc, self.lse_acc, stream)
+        for kc, vc, ko in zip(k_chunks, v_chunks, k_offsets):
+            attn_fwd(self.q, kc, vc, self.blk, self.lse_blk, self.scale,
+                     self.causal, -1, -1, self.q_offset, ko, stream)
+            attn_merge(self.acc, self.lse_acc, self.blk, self.lse_blk, stream)
+        attn_acc_cast(self.acc, self.out, stream)
+        return self.out, self.lse_acc
+
+
+def ring_share(q, k_chunks, v_chunks, k_offsets, q_offset, scale=None,
+               causal=True, stream=None):
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return RingShare(q, scale, causal, q_offset).run(k_chunks, v_chunks,
+                                                     k_offsets, stream)

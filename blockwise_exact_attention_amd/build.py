@@ -1,0 +1,74 @@
+"""Build libattn.so (the C-ABI attention library) for gfx950 with hipcc.
+
+    python -m blockwise_exact_attention_amd.build
+
+Compiles every csrc/*.hip translation unit and links them into
+blockwise_exact_attention_amd/libattn.so (in-tree, so it travels with the
+source tree).  Device code is built with packed-fp32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import concurrent.futures as cf
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libattn.so")
+OBJDIR = os.path.join(ROOT, "_build")
+
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def _hipcc():
+    cand = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(cand):
+        raise RuntimeError("hipcc not found; cannot build libattn.so")
+    return cand
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip"))
+
+
+def _compile(src, hipcc):
+    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+    cmd = [hipcc, *FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose=True):
+    """Compile and link libattn.so; always rebuilds."""
+    hipcc = _hipcc()
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, hipcc), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,230 @@
+// C ABI of the attention library: argument checks, mask-bound folding and
+// dispatch.  Every check runs before the first HIP call, so a rejected call
+// launches nothing and touches no device state.
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "launch.hpp"
+
+namespace {
+
+using bea::AttnShape;
+
+bool sizes_ok(long long a, long long b, long long c, long long d) {
+  if (a <= 0 || b <= 0 || c <= 0 || d <= 0) return false;
+  // every element count (and its byte size) must stay far below 2^62
+  const long long lim = 1LL << 58;
+  if (a > lim / b) return false;
+  const long long ab = a * b;
+  if (ab > lim / c) return false;
+  const long long abc = ab * c;
+  return abc <= lim / d;
+}
+
+bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, long long bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int32_t sat32(long long x) {
+  if (x < INT_MIN) return INT_MIN;
+  if (x > INT_MAX) return INT_MAX;
+  return (int32_t)x;
+}
+
+// Fold causal, the window and the offsets into bounds on j - i:
+// key j is allowed for row i iff dlo <= j - i <= dhi.  With
+// delta = q_offset - k_offset: causal kpos <= qpos is j - i <= delta, the
+// window qpos - win_l <= kpos <= qpos + win_r is
+// delta - win_l <= j - i <= delta + win_r.  |delta| is clamped to 2^40 first:
+// |j - i| < 2^31, so larger values give the same answer, and the sums below
+// cannot overflow.  Saturating to int32 keeps every comparison exact.
+void mask_bounds(int causal, int win_l, int win_r, long long q_offset,
+                 long long k_offset, int* dlo, int* dhi) {
+  const long long cap = 1LL << 40;
+  long long qo = q_offset, ko = k_offset;
+  // q_offset - k_offset without overflow, clamped
+  long long delta;
+  if (qo >= 0 && ko < 0 && qo > LLONG_MAX + ko) delta = cap;
+  else if (qo < 0 && ko > 0 && qo < LLONG_MIN + ko) delta = -cap;
+  else delta = qo - ko;
+  if (delta > cap) delta = cap;
+  if (delta < -cap) delta = -cap;
+  long long lo = LLONG_MIN / 2, hi = LLONG_MAX / 2;
+  if (causal) hi = delta;
+  if (win_r >= 0 && delta + win_r < hi) hi = delta + win_r;
+  if (win_l >= 0) lo = delta - win_l;
+  *dlo = sat32(lo);
+  *dhi = sat32(hi);
+}
+
+int check_attn_args(int n, int l_q, int l_k, int h, int h_kv, int d,
+                    float scale, int dtype) {
+  if (!sizes_ok(n, l_q, h, d) || !sizes_ok(n, l_k, h_kv, d))
+    return ATTN_ERR_SHAPE;
+  if (h % h_kv != 0) return ATTN_ERR_SHAPE;
+  // grid size (q tiles x heads) must fit a 32-bit launch
+  if ((long long)((l_q + 63) / 64) * n * h > INT_MAX) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
+             int causal, int win_l, int win_r, long long q_offset,
+             long long k_offset, void* stream, int dtype) {
+  if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL;
+  int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(out, 16) || !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
+  const long long es = dtype == ATTN_BF16 ? 2 : 4;
+  const long long qb = (long long)n * l_q * h * d * es;
+  const long long kb = (long long)n * l_k * h_kv * d * es;
+  const long long lb = (long long)n * h * l_q * 4;
+  const Range rq = range(q, qb), rk = range(k, kb), rv = range(v, kb),
+              ro = range(out, qb), rl = range(lse, lb);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) ||
+      overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ro))
+    return ATTN_ERR_ALIAS;
+
+  AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+  mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  return finish(dtype == ATTN_BF16 ? bea::launch_fwd_bf16(q, k, v, out, lse, s, hs)
+                                   : bea::launch_fwd_f32(q, k, v, out, lse, s, hs));
+}
+
+int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
+               const float* lse_blk, int n, int l, int h, int d, int blk_dtype,
+               void* stream) {
+  if (!out_acc || !lse_acc || !out_blk || !lse_blk) return ATTN_ERR_NULL;
+  if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;
+  if (blk_dtype != ATTN_F32 && blk_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(out_acc, 16) || !aligned(out_blk, 16) || !aligned(lse_acc, 4) ||
+      !aligned(lse_blk, 4))
+    return ATTN_ERR_ALIGN;
+  const long long es = blk_dtype == ATTN_BF16 ? 2 : 4;
+  const long long ne = (long long)n * l * h * d;
+  const long long nr = (long long)n * l * h;
+  const Range ra = range(out_acc, ne * 4), rla = range(lse_acc, nr * 4),
+              rb = range(out_blk, ne * es), rlb = range(lse_blk, nr * 4);
+  if (overlap(ra, rla) || overlap(ra, rb) || overlap(ra, rlb) ||
+      overlap(rla, rb) || overlap(rla, rlb))
+    return ATTN_ERR_ALIAS;
+  (void)hipGetLastError();
+  return finish(bea::launch_merge(out_acc, lse_acc, out_blk, lse_blk, n, l, h,
+                                  d, blk_dtype == ATTN_BF16,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int attn_acc_init(float* out_acc, float* lse_acc, int n, int l, int h, int d,
+                  void* stream) {
+  if (!out_acc || !lse_acc) return ATTN_ERR_NULL;
+  if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;
+  if (!aligned(out_acc, 4) || !aligned(lse_acc, 4)) return ATTN_ERR_ALIGN;
+  const long long ne = (long long)n * l * h * d;
+  const long long nr = (long long)n * l * h;
+  if (overlap(range(out_acc, ne * 4), range(lse_acc, nr * 4)))
+    return ATTN_ERR_ALIAS;
+  (void)hipGetLastError();
+  return finish(bea::launch_acc_init(out_acc, lse_acc, n, l, h, d,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int attn_acc_cast(const float* out_acc, void* out, int n, int l, int h, int d,
+                  int dtype, void* stream) {
+  if (!out_acc || !out) return ATTN_ERR_NULL;
+  if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(out_acc, 16) || !aligned(out, 16)) return ATTN_ERR_ALIGN;
+  const long long ne = (long long)n * l * h * d;
+  const long long es = dtype == ATTN_BF16 ? 2 : 4;
+  if (overlap(range(out_acc, ne * 4), range(out, ne * es))) return ATTN_ERR_ALIAS;
+  (void)hipGetLastError();
+  return finish(bea::launch_acc_cast(out_acc, out, n, l, h, d,
+                                     dtype == ATTN_BF16,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv,
+                                int d) {
+  if (!sizes_ok(n, l_q, h, d) || !sizes_ok(n, l_k, h_kv, d)) return 0;
+  if (h % h_kv != 0) return 0;
+  return bea::bwd_workspace_bytes(n, l_q, h);
+}
+
+int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
+             const void* out, const float* lse, void* dq, void* dk, void* dv,
+             int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
+             int causal, int win_l, int win_r, long long q_offset,
+             long long k_offset, void* workspace, size_t workspace_bytes,
+             void* stream, int dtype) {
+  if (!dout || !q || !k || !v || !out || !lse || !dq || !dk || !dv)
+    return ATTN_ERR_NULL;
+  int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = bea::bwd_workspace_bytes(n, l_q, h);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) ||
+      !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(workspace, 16))
+    return ATTN_ERR_ALIGN;
+  const long long es = dtype == ATTN_BF16 ? 2 : 4;
+  const long long qb = (long long)n * l_q * h * d * es;
+  const long long kb = (long long)n * l_k * h_kv * d * es;
+  const long long lb = (long long)n * h * l_q * 4;
+  const Range ins[] = {range(dout, qb), range(q, qb), range(k, kb),
+                       range(v, kb), range(out, qb), range(lse, lb)};
+  const Range outs[] = {range(dq, qb), range(dk, kb), range(dv, kb),
+                        range(workspace, (long long)need)};
+  for (int a = 0; a < 4; ++a) {
+    for (const Range& r : ins)
+      if (overlap(outs[a], r)) return ATTN_ERR_ALIAS;
+    for (int c = a + 1; c < 4; ++c)
+      if (overlap(outs[a], outs[c])) return ATTN_ERR_ALIAS;
+  }
+  AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+  mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
+  (void)hipGetLastError();
+  return finish(bea::launch_bwd(dout, q, k, v, out, lse, dq, dk, dv, s,
+                                workspace, dtype == ATTN_BF16,
+                                static_cast<hipStream_t>(stream)));
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid sizes (<= 0, h % h_kv != 0, or too large)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim, dtype or scale";
+    case ATTN_ERR_HIP: return "HIP launch failure";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_ALIAS: return "an output overlaps another buffer";
+    case ATTN_ERR_ALIGN: return "misaligned tensor pointer";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

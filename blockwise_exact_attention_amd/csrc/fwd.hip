@@ -1,0 +1,522 @@
+// Exact attention forward for gfx950: blockwise over key tiles with an online
+// softmax, bf16 MFMA with fp32 accumulation (and an fp32 SIMT variant).
+//
+// What is computed follows the pages "picotron/parallel/context_parallel.py"
+// (ring_attention_forward: S = scale * Q K^T, causal mask, LSE = log sum exp,
+// O = softmax(S) V; RingAttention._repeat_kv for grouped heads) and
+// "flash_sharding.py" (ring_fwd: the (O, LSE) pair per query row, a row with
+// no allowed key gives O = 0 and LSE = -inf; the log1p merge, which the
+// online softmax applies per key tile).
+//
+// bf16 kernel layout (one workgroup = 4 waves = 128 query rows of one head):
+//  * Each wave owns 32 query rows.  Scores are computed transposed,
+//    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows come from LDS as the
+//    A operand, the wave's Q rows stay in VGPRs as the B operand for the whole
+//    key loop.  In the result every lane holds one query (lane % 32) and 16
+//    keys per 32-key block, so a row max needs one cross-half exchange and a
+//    row sum none until the epilogue.
+//  * O^T = V^T P^T reuses the S^T registers directly as the B operand (the
+//    contraction order over keys is free, so the 8 keys a lane holds become
+//    the 8 k-slots it supplies).  V is stored transposed in LDS with keys
+//    permuted inside each 16-key group so that the matching A operand is one
+//    16-byte LDS read.
+//  * Key tiles wholly outside a workgroup's causal/window band are never
+//    visited; tiles wholly inside run without per-element mask work.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bea {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;   // query rows per workgroup
+constexpr int kThreads = 64 * kWaves;
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int l_q, l_k, h, h_kv, grp;
+  int n_heads;     // n * h
+  int n_qtiles;
+  int xcd_groups;  // 1: keep the workgroups of one key/value head on one XCD
+  int reverse;     // 1: launch the last (longest, under causal) q tiles first
+  float c;         // scale * log2(e)
+  int dlo, dhi;
+};
+
+// blockIdx.x -> (q tile, flattened head b*h + hq).
+//
+// Workgroups are handed to the 8 XCDs round-robin by id, and each XCD has its
+// own L2.  When the key/value groups split evenly over the XCDs, every
+// workgroup that reads one key/value head is given an id of the same residue
+// mod 8, so that head's K/V tiles are fetched into one L2 only.  Under causal
+// masking the last q tiles see the most keys; they get the lowest ids.
+__device__ __forceinline__ void map_block(const FwdParams& p, int& tile,
+                                          int& head) {
+  const int w = blockIdx.x;
+  int rank;
+  if (p.xcd_groups) {
+    const int xcd = w & 7;
+    const int slot = w >> 3;
+    const int per_xcd = p.n_heads >> 3;
+    rank = slot / per_xcd;
+    const int rem = slot - rank * per_xcd;
+    const int gi = rem / p.grp;
+    const int in_group = rem - gi * p.grp;
+    head = (xcd + 8 * gi) * p.grp + in_group;
+  } else {
+    rank = w / p.n_heads;
+    head = w - rank * p.n_heads;
+  }
+  tile = p.reverse ? (p.n_qtiles - 1 - rank) : rank;
+}
+
+template <int D, int BN>
+struct FwdSmem {
+  static constexpr int kKStride = D + 8;   // bf16 per K row (16 B pad)
+  static constexpr int kVStride = BN + 8;  // bf16 per V^T row (16 B pad)
+  uint16_t k[BN * kKStride];
+  uint16_t vt[D * kVStride];
+};
+
+// Position of key kk (0..BN-1) inside a V^T row: within each group of 16 keys
+// bits 2 and 3 swap, so that keys {4h+0..3, 8+4h+0..3} (what a lane of half h
+// holds after the S^T MFMA) are 8 contiguous elements.
+__device__ __forceinline__ int vt_pos(int kk) {
+  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+template <int D, int BN, bool NEGS>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
+  static_assert(BN * D / 32 == kThreads, "one V group of 4 keys x 8 dims per thread");
+  static_assert((BN * D / 8) % kThreads == 0, "whole K chunks per thread");
+  constexpr int KS = FwdSmem<D, BN>::kKStride;
+  constexpr int VS = FwdSmem<D, BN>::kVStride;
+  constexpr int KCH = BN * D / 8 / kThreads;
+  constexpr int NKB = BN / 32;   // 32-key blocks per tile
+  constexpr int NDS = D / 16;    // 16-wide dim slices (S^T MFMA k steps)
+  constexpr int NDB = D / 32;    // 32-dim blocks of O^T
+  constexpr int NPS = BN / 16;   // 16-key slices (O^T MFMA k steps)
+
+  __shared__ FwdSmem<D, BN> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  int tile, head;
+  map_block(p, tile, head);
+  const int b = head / p.h;
+  const int hq = head - b * p.h;
+  const int g = hq / p.grp;
+
+  const int last_row = p.l_q - 1;
+  const int i0 = tile * kBM;
+  const int iw = i0 + wave * 32;
+  const int qi = iw + col;
+
+  // Key-tile range of the workgroup (rows i0 .. min(i0+kBM, l_q)-1).
+  const long long jlo = max(0LL, (long long)i0 + p.dlo);
+  const long long jhi = min((long long)p.l_k - 1,
+                            (long long)min(i0 + kBM - 1, last_row) + p.dhi);
+  int kt_begin = 0, kt_end = 0;
+  if (jlo <= jhi) {
+    kt_begin = (int)(jlo / BN);
+    kt_end = (int)(jhi / BN) + 1;
+  }
+  // Key range of this wave.
+  const int wa = iw;
+  const int wb = min(iw + 31, last_row);
+  const bool wave_live = wa <= last_row;
+  const long long wjlo = max(0LL, (long long)wa + p.dlo);
+  const long long wjhi = min((long long)p.l_k - 1, (long long)wb + p.dhi);
+
+  // Q fragment: B operand of S^T = K Q^T, resident for the whole loop.
+  const size_t q_row = (size_t)p.h * D;
+  const uint16_t* qptr = p.q + ((size_t)b * p.l_q + min(qi, last_row)) * q_row +
+                         (size_t)hq * D + 8 * half;
+  u32x4_t qf[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s)
+    qf[s] = *reinterpret_cast<const u32x4_t*>(qptr + 16 * s);
+
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m = kNegInf;  // running row max in log2 units (scale*log2e*s)
+  float lsum = 0.f;   // this lane's half of the running row sum
+
+  const size_t kv_row = (size_t)p.h_kv * D;
+  const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
+  const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
+
+  // Register staging of the next tile (global -> VGPR -> LDS).
+  u32x4_t kreg[KCH];
+  u32x4_t vreg[4];
+  const int vg_key = (tid / (D / 8)) * 4;  // first of this thread's 4 V keys
+  const int vg_c8 = tid % (D / 8);         // its 8-dim chunk
+
+  auto gload = [&](int kt) {
+    const int j0 = kt * BN;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int id = tid + c * kThreads;
+      const int row = id / (D / 8);
+      const int c8 = id % (D / 8);
+      const int j = min(j0 + row, p.l_k - 1);
+      kreg[c] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)j * kv_row + c8 * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = min(j0 + vg_key + r, p.l_k - 1);
+      vreg[r] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)j * kv_row + vg_c8 * 8);
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int id = tid + c * kThreads;
+      const int row = id / (D / 8);
+      const int c8 = id % (D / 8);
+      *reinterpret_cast<u32x4_t*>(&sm.k[row * KS + c8 * 8]) = kreg[c];
+    }
+    const int pos = vt_pos(vg_key);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int w = dd >> 1;
+      const int sh = (dd & 1) * 16;
+      const uint32_t e0 = (vreg[0][w] >> sh) & 0xffffu;
+      const uint32_t e1 = (vreg[1][w] >> sh) & 0xffffu;
+      const uint32_t e2 = (vreg[2][w] >> sh) & 0xffffu;
+      const uint32_t e3 = (vreg[3][w] >> sh) & 0xffffu;
+      u32x2_t pk;
+      pk[0] = e0 | (e1 << 16);
+      pk[1] = e2 | (e3 << 16);
+      *reinterpret_cast<u32x2_t*>(&sm.vt[(vg_c8 * 8 + dd) * VS + pos]) = pk;
+    }
+  };
+
+  if (kt_begin < kt_end) {
+    gload(kt_begin);
+    sstore();
+  }
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    __syncthreads();
+    if (kt + 1 < kt_end) gload(kt + 1);
+    const int j0 = kt * BN;
+    const bool live = wave_live && (long long)j0 <= wjhi &&
+                      (long long)(j0 + BN - 1) >= wjlo;
+    if (live) {
+      const bool full = (j0 + BN <= p.l_k) &&
+                        ((long long)j0 - wb >= p.dlo) &&
+                        ((long long)(j0 + BN - 1) - wa <= p.dhi);
+      // ---- S^T = K Q^T for the tile: NKB blocks of 32 keys x 32 queries
+      f32x16_t sacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+              &sm.k[(32 * kb + col) * KS + 16 * s + 8 * half]);
+          sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
+        }
+      }
+      if (NEGS) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = -sacc[kb][r];
+      }
+      // ---- mask (boundary tiles only) and row max
+      float mx = kNegInf;
+      if (full) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int rel = j - qi;
+            const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
+            sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+            mx = fmaxf(mx, sacc[kb][r]);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mt = (mx == kNegInf) ? kNegInf : mx * p.c;
+      const float mnew = fmaxf(m, mt);
+      const float muse = (mnew == kNegInf) ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m - muse);
+      m = mnew;
+      // ---- P = exp2(c*s - m) packed to bf16 as the B operand of O^T += V^T P^T
+      u32x4_t pf[NPS];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, -muse));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.c, -muse));
+          if (!full) {
+            p0 = (sacc[kb][r] == kNegInf) ? 0.f : p0;
+            p1 = (sacc[kb][r + 1] == kNegInf) ? 0.f : p1;
+          }
+          rs += p0 + p1;
+          pf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+        }
+      lsum = lsum * alpha + rs;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int t = 0; t < NPS; ++t)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+              &sm.vt[(32 * db + col) * VS + 16 * t + 8 * half]);
+          oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
+        }
+    }
+    __syncthreads();
+    if (kt + 1 < kt_end) sstore();
+  }
+
+  // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (qi <= last_row) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    uint16_t* optr = p.o + ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = 32 * db + 8 * r4 + 4 * half;
+        u32x2_t w;
+        w[0] = pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(optr + dim) = w;
+      }
+    if (half == 0) {
+      const float muse = (m == kNegInf) ? 0.f : m;
+      p.lse[(size_t)head * p.l_q + qi] =
+          ltot > 0.f ? (muse + __log2f(ltot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+//
+// fp32 inputs: a SIMT kernel (fp32 FMA), 64 query rows per workgroup, four
+// lanes per row each owning D/4 dims (float4 chunks c, c+4, c+8, ...).  Keys
+// are staged 64 at a time in LDS and consumed in groups of 16 with the same
+// online-softmax update as the bf16 kernel.
+struct FwdF32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int l_q, l_k, h, h_kv, grp;
+  int n_heads;
+  float c;
+  int dlo, dhi;
+};
+
+constexpr int kF32Rows = 64;
+constexpr int kF32Keys = 64;
+
+template <int D, bool NEGS>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdF32Params p) {
+  constexpr int NC = D / 16;  // float4 chunks per lane
+  __shared__ f32x4_t ks[kF32Keys * (D / 4)];
+  __shared__ f32x4_t vs[kF32Keys * (D / 4)];
+
+  const int tid = threadIdx.x;
+  const int c = tid & 3;
+  const int row = tid >> 2;
+  const int tile = blockIdx.x / p.n_heads;
+  const int head = blockIdx.x - tile * p.n_heads;
+  const int b = head / p.h;
+  const int hq = head - b * p.h;
+  const int g = hq / p.grp;
+  const int last_row = p.l_q - 1;
+  const int i0 = tile * kF32Rows;
+  const int qi = i0 + row;
+
+  const long long jlo = max(0LL, (long long)i0 + p.dlo);
+  const long long jhi = min((long long)p.l_k - 1,
+                            (long long)min(i0 + kF32Rows - 1, last_row) + p.dhi);
+
+  const size_t q_row = (size_t)p.h * D;
+  const f32x4_t* qptr = reinterpret_cast<const f32x4_t*>(
+      p.q + ((size_t)b * p.l_q + min(qi, last_row)) * q_row + (size_t)hq * D);
+  f32x4_t qv[NC];
+  f32x4_t ov[NC];
+#pragma unroll
+  for (int m4 = 0; m4 < NC; ++m4) {
+    qv[m4] = qptr[c + 4 * m4];
+    ov[m4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float m = kNegInf, lsum = 0.f;
+
+  const size_t kv_row = (size_t)p.h_kv * D;
+  const float* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
+  const float* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
+
+  if (jlo <= jhi) {
+    for (long long j0 = (jlo / kF32Keys) * kF32Keys; j0 <= jhi; j0 += kF32Keys) {
+      __syncthreads();
+      for (int e = tid; e < kF32Keys * (D / 4); e += 256) {
+        const int kr = e / (D / 4);
+        const int c4 = e - kr * (D / 4);
+        const long long j = min(j0 + kr, (long long)p.l_k - 1);
+        ks[e] = reinterpret_cast<const f32x4_t*>(kbase + (size_t)j * kv_row)[c4];
+        vs[e] = reinterpret_cast<const f32x4_t*>(vbase + (size_t)j * kv_row)[c4];
+      }
+      __syncthreads();
+      for (int jg = 0; jg < kF32Keys; jg += 16) {
+        float s[16];
+        float mx = kNegInf;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          float acc = 0.f;
+#pragma unroll
+          for (int m4 = 0; m4 < NC; ++m4) {
+            const f32x4_t kk = ks[(jg + jj) * (D / 4) + c + 4 * m4];
+            acc = fmaf(qv[m4][0], kk[0], acc);
+            acc = fmaf(qv[m4][1], kk[1], acc);
+            acc = fmaf(qv[m4][2], kk[2], acc);
+            acc = fmaf(qv[m4][3], kk[3], acc);
+          }
+          acc += __shfl_xor(acc, 1);
+          acc += __shfl_xor(acc, 2);
+          if (NEGS) acc = -acc;
+          const long long j = j0 + jg + jj;
+          const long long rel = j - qi;
+          const bool ok = j < p.l_k && rel >= p.dlo && rel <= p.dhi;
+          s[jj] = ok ? acc : kNegInf;
+          mx = fmaxf(mx, s[jj]);
+        }
+        const float mt = (mx == kNegInf) ? kNegInf : mx * p.c;
+        const float mnew = fmaxf(m, mt);
+        const float muse = (mnew == kNegInf) ? 0.f : mnew;
+        const float alpha = exp2f(m - muse);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int m4 = 0; m4 < NC; ++m4) ov[m4] *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const float pj = (s[jj] == kNegInf) ? 0.f : exp2f(fmaf(s[jj], p.c, -muse));
+          lsum += pj;
+#pragma unroll
+          for (int m4 = 0; m4 < NC; ++m4) {
+            const f32x4_t vv = vs[(jg + jj) * (D / 4) + c + 4 * m4];
+            ov[m4][0] = fmaf(pj, vv[0], ov[m4][0]);
+            ov[m4][1] = fmaf(pj, vv[1], ov[m4][1]);
+            ov[m4][2] = fmaf(pj, vv[2], ov[m4][2]);
+            ov[m4][3] = fmaf(pj, vv[3], ov[m4][3]);
+          }
+        }
+      }
+    }
+  }
+  if (qi <= last_row) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    f32x4_t* optr = reinterpret_cast<f32x4_t*>(
+        p.o + ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D);
+#pragma unroll
+    for (int m4 = 0; m4 < NC; ++m4) optr[c + 4 * m4] = ov[m4] * inv;
+    if (c == 0) {
+      const float muse = (m == kNegInf) ? 0.f : m;
+      p.lse[(size_t)head * p.l_q + qi] =
+          lsum > 0.f ? (muse + log2f(lsum)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
+                           void* out, float* lse, const AttnShape& s,
+                           hipStream_t stream) {
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.l_q = s.l_q;
+  p.l_k = s.l_k;
+  p.h = s.h;
+  p.h_kv = s.h_kv;
+  p.grp = s.h / s.h_kv;
+  p.n_heads = s.n * s.h;
+  p.n_qtiles = (s.l_q + kBM - 1) / kBM;
+  p.xcd_groups = ((s.n * s.h_kv) % 8 == 0) ? 1 : 0;
+  p.reverse = s.causal ? 1 : 0;
+  p.c = fabsf(s.scale) * kLog2e;
+  p.dlo = s.dlo;
+  p.dhi = s.dhi;
+  const bool negs = s.scale < 0.f;
+  dim3 grid((unsigned)p.n_qtiles * (unsigned)p.n_heads);
+  dim3 block(kThreads);
+  if (s.d == 128) {
+    if (negs) hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, false>), grid, block, 0, stream, p);
+  } else {
+    if (negs) hipLaunchKernelGGL((fwd_bf16_kernel<64, 128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 128, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
+                          void* out, float* lse, const AttnShape& s,
+                          hipStream_t stream) {
+  FwdF32Params p;
+  p.q = static_cast<const float*>(q);
+  p.k = static_cast<const float*>(k);
+  p.v = static_cast<const float*>(v);
+  p.o = static_cast<float*>(out);
+  p.lse = lse;
+  p.l_q = s.l_q;
+  p.l_k = s.l_k;
+  p.h = s.h;
+  p.h_kv = s.h_kv;
+  p.grp = s.h / s.h_kv;
+  p.n_heads = s.n * s.h;
+  p.c = fabsf(s.scale) * kLog2e;
+  p.dlo = s.dlo;
+  p.dhi = s.dhi;
+  const bool negs = s.scale < 0.f;
+  const unsigned tiles = (unsigned)((s.l_q + kF32Rows - 1) / kF32Rows);
+  dim3 grid(tiles * (unsigned)p.n_heads);
+  dim3 block(256);
+  if (s.d == 128) {
+    if (negs) hipLaunchKernelGGL((fwd_f32_kernel<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_f32_kernel<128, false>), grid, block, 0, stream, p);
+  } else {
+    if (negs) hipLaunchKernelGGL((fwd_f32_kernel<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_f32_kernel<64, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bea

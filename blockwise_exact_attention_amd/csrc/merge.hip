@@ -1,0 +1,196 @@
+// The (O, LSE) merge of partial attention results and the ring accumulator's
+// set-up and final cast, for gfx950.  All three are elementwise and bound by
+// HBM bandwidth.
+//
+// Sources: "flash_sharding.py" (flash_attn_jax), ring_fwd - accumulator
+// starts at O = 0 (fp32) and LSE = -inf; each chunk's O is upcast to fp32 and
+// merged as lse = max + log1p(exp(min - max)),
+// o = o1 exp(lse1 - lse) + o2 exp(lse2 - lse); the result is cast back to the
+// query dtype at the end.  "picotron/parallel/context_parallel.py",
+// update_out_and_lse - the same merge in sigmoid form, and the first block
+// simply becomes the accumulator (here: whenever the accumulator's LSE is
+// -inf).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bea {
+namespace {
+
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxRows = 256;
+
+// Row modes: 0 keep the accumulator, 1 take the block, 2 weighted sum.
+template <bool BLK_BF16>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    float* __restrict__ acc, float* __restrict__ lse_acc,
+    const void* __restrict__ blk, const float* __restrict__ lse_blk, int l,
+    int h, int d, long long rows_total, int rows_per_block) {
+  __shared__ float s_wa[kMergeMaxRows];
+  __shared__ float s_wb[kMergeMaxRows];
+  __shared__ int s_mode[kMergeMaxRows];
+
+  const long long r0 = (long long)blockIdx.x * rows_per_block;
+  const int nr = (int)min((long long)rows_per_block, rows_total - r0);
+  const int tid = threadIdx.x;
+
+  if (tid < nr) {
+    // rows are ordered (b, i, hq) like O; the LSE of that row sits at
+    // [b, hq, i]
+    const long long row = r0 + tid;
+    const long long bi = row / h;
+    const int hq = (int)(row - bi * h);
+    const long long b = bi / l;
+    const int i = (int)(bi - b * l);
+    const size_t li = ((size_t)b * h + hq) * l + i;
+    const float a = lse_acc[li];
+    const float bb = lse_blk[li];
+    int mode;
+    float wa = 0.f, wb = 0.f;
+    if (bb == kNegInf) {
+      mode = 0;
+    } else if (a == kNegInf) {
+      mode = 1;
+      lse_acc[li] = bb;
+    } else {
+      mode = 2;
+      const float mx = fmaxf(a, bb);
+      const float mn = fminf(a, bb);
+      const float lse = mx + log1pf(expf(mn - mx));
+      wa = expf(a - lse);
+      wb = expf(bb - lse);
+      lse_acc[li] = lse;
+    }
+    s_mode[tid] = mode;
+    s_wa[tid] = wa;
+    s_wb[tid] = wb;
+  }
+  __syncthreads();
+
+  const size_t e0 = (size_t)r0 * d;
+  const int ne = nr * d;
+  if ((d & 3) == 0) {
+    for (int e = tid * 4; e < ne; e += kMergeThreads * 4) {
+      const int rr = e / d;
+      const int mode = s_mode[rr];
+      if (mode == 0) continue;
+      f32x4_t bv;
+      if (BLK_BF16) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(
+            static_cast<const uint16_t*>(blk) + e0 + e);
+        bv = f32x4_t{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+      } else {
+        bv = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(blk) + e0 + e);
+      }
+      f32x4_t* ap = reinterpret_cast<f32x4_t*>(acc + e0 + e);
+      if (mode == 1) {
+        *ap = bv;
+      } else {
+        const f32x4_t av = *ap;
+        *ap = av * s_wa[rr] + bv * s_wb[rr];
+      }
+    }
+  } else {
+    for (int e = tid; e < ne; e += kMergeThreads) {
+      const int rr = e / d;
+      const int mode = s_mode[rr];
+      if (mode == 0) continue;
+      const float bv = BLK_BF16
+          ? bf16_lo(static_cast<const uint16_t*>(blk)[e0 + e])
+          : static_cast<const float*>(blk)[e0 + e];
+      acc[e0 + e] = (mode == 1) ? bv : acc[e0 + e] * s_wa[rr] + bv * s_wb[rr];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void acc_init_kernel(float* __restrict__ acc,
+                                                       float* __restrict__ lse,
+                                                       long long n_acc,
+                                                       long long n_lse) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n_acc;
+       e += stride)
+    acc[e] = 0.f;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n_lse;
+       e += stride)
+    lse[e] = kNegInf;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void acc_cast_kernel(const float* __restrict__ acc,
+                                                       void* __restrict__ out,
+                                                       long long n_elem) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long n4 = n_elem / 4;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n4;
+       e += stride) {
+    const f32x4_t x = reinterpret_cast<const f32x4_t*>(acc)[e];
+    if (BF16) {
+      u32x2_t w;
+      w[0] = pack_bf16x2(x[0], x[1]);
+      w[1] = pack_bf16x2(x[2], x[3]);
+      reinterpret_cast<u32x2_t*>(out)[e] = w;
+    } else {
+      reinterpret_cast<f32x4_t*>(out)[e] = x;
+    }
+  }
+  for (long long e = n4 * 4 + (long long)blockIdx.x * blockDim.x + threadIdx.x;
+       e < n_elem; e += stride) {
+    if (BF16) {
+      const uint32_t w = pack_bf16x2(acc[e], 0.f);
+      static_cast<uint16_t*>(out)[e] = (uint16_t)(w & 0xffffu);
+    } else {
+      static_cast<float*>(out)[e] = acc[e];
+    }
+  }
+}
+
+unsigned grid_for(long long work, int per_block) {
+  long long g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
+                        const float* lse_blk, int n, int l, int h, int d,
+                        bool blk_bf16, hipStream_t stream) {
+  const long long rows = (long long)n * l * h;
+  int rpb = 1024 / d;
+  if (rpb < 1) rpb = 1;
+  if (rpb > kMergeMaxRows) rpb = kMergeMaxRows;
+  const long long blocks = (rows + rpb - 1) / rpb;
+  dim3 grid((unsigned)blocks), block(kMergeThreads);
+  if (blk_bf16)
+    hipLaunchKernelGGL((merge_kernel<true>), grid, block, 0, stream, out_acc,
+                       lse_acc, out_blk, lse_blk, l, h, d, rows, rpb);
+  else
+    hipLaunchKernelGGL((merge_kernel<false>), grid, block, 0, stream, out_acc,
+                       lse_acc, out_blk, lse_blk, l, h, d, rows, rpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_acc_init(float* out_acc, float* lse_acc, int n, int l, int h,
+                           int d, hipStream_t stream) {
+  const long long n_acc = (long long)n * l * h * d;
+  const long long n_lse = (long long)n * l * h;
+  hipLaunchKernelGGL(acc_init_kernel, dim3(grid_for(n_acc, 256 * 4)), dim3(256),
+                     0, stream, out_acc, lse_acc, n_acc, n_lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_acc_cast(const float* out_acc, void* out, int n, int l,
+                           int h, int d, bool bf16, hipStream_t stream) {
+  const long long n_elem = (long long)n * l * h * d;
+  dim3 grid(grid_for(n_elem / 4 + 1, 256 * 2)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL((acc_cast_kernel<true>), grid, block, 0, stream, out_acc,
+                       out, n_elem);
+  else
+    hipLaunchKernelGGL((acc_cast_kernel<false>), grid, block, 0, stream, out_acc,
+                       out, n_elem);
+  return hipGetLastError();
+}
+
+}  // namespace bea

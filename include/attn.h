@@ -1,0 +1,166 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) blockwise exact-attention library.
+ *
+ * Exact scaled-dot-product attention computed blockwise with an online
+ * softmax, returning both the output O and the natural-log log-sum-exp LSE of
+ * every query row; the (O, LSE) merge of partial results; the accumulator
+ * set-up and final cast of one device's ring-attention share; and the
+ * backward pass.
+ *
+ * Sources (page title, then the function on the page):
+ *   - "flash_sharding.py" (flash_attn_jax): partition_fwd / partition_bwd
+ *     (the kernel interface fwd(q,k,v; softmax_scale, is_causal,
+ *     window_size) -> (o, lse) and bwd(do,q,k,v,o,lse; ...) -> (dq,dk,dv);
+ *     O sharded like q, LSE laid out [n,h,l]); ring_fwd (accumulator start
+ *     O = 0, LSE = -inf; skipped chunk = (0, -inf); log1p merge; final cast
+ *     of O to the query dtype); ring_bwd (gradients cast to the query dtype).
+ *   - "picotron/parallel/context_parallel.py": ring_attention_forward and
+ *     ring_attention_backward (the math), update_out_and_lse (merge; block
+ *     output upcast to fp32), RingAttention._repeat_kv (grouped-query heads).
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is device memory owned by the caller.  The library
+ *     allocates nothing, frees nothing and keeps no pointer after the call
+ *     returns.  All tensors are dense and row-major (contiguous).
+ *   - Layouts: q, out, dout, dq        [n, l_q, h,    d]
+ *              k, v, dk, dv            [n, l_k, h_kv, d]
+ *              lse                     [n, h, l_q]   float32
+ *              out_acc                 [n, l, h, d]  float32
+ *   - dtype selects the element type of q, k, v, out, dout, dq, dk, dv:
+ *     ATTN_BF16 (bfloat16) or ATTN_F32 (float32).  LSE and the merge
+ *     accumulator are always float32.  Outputs are rounded to nearest even.
+ *   - Grouped-query heads: h must be a multiple of h_kv and query head hq
+ *     reads key/value head hq / (h / h_kv) (consecutive query heads share a
+ *     key/value head).  h_kv == 1 is multi-query attention.
+ *   - Masking uses absolute positions qpos = q_offset + i for query row i and
+ *     kpos = k_offset + j for key row j.  Key j is allowed for row i when
+ *       (causal == 0 || kpos <= qpos) &&
+ *       (win_l < 0 || kpos >= qpos - win_l) &&
+ *       (win_r < 0 || kpos <= qpos + win_r).
+ *     Window bounds are inclusive; a negative side is unbounded, so
+ *     (win_l, win_r) = (-1, -1) means no window.  Only q_offset - k_offset
+ *     matters.  Offsets 0 give top-left causal alignment.
+ *   - A query row with no allowed key gets O = 0 and LSE = -inf, and zero
+ *     gradients.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues work on it and returns without synchronising.  The
+ *     library keeps no global state: calls on different streams from
+ *     different host threads are independent.
+ *   - Every argument is checked before any HIP call; on error nothing is
+ *     launched and a nonzero status is returned.  ATTN_ERR_HIP reports a
+ *     failed launch (hipGetLastError after the launch).
+ */
+#ifndef BLOCKWISE_EXACT_ATTENTION_AMD_ATTN_H
+#define BLOCKWISE_EXACT_ATTENTION_AMD_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  ATTN_ERR_SHAPE = 2,       /* a size is <= 0, h % h_kv != 0, or sizes overflow  */
+  ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite or
+                               negative scale                                    */
+  ATTN_ERR_HIP = 4,         /* the HIP runtime reported a launch failure         */
+  ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
+  ATTN_ERR_ALIAS = 6,       /* an input buffer overlaps an output buffer         */
+  ATTN_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned (LSE
+                               pointers: 4-byte aligned)                          */
+};
+
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/*
+ * attn_fwd - exact attention forward, blockwise with an online softmax.
+ * (flash_sharding.py: the fwd kernel called by partition_fwd and ring_fwd;
+ *  picotron: ring_attention_forward.)
+ *
+ *   O[b,i,hq,:] = sum_j P_ij v[b,j,g,:],  P_ij = exp(s_ij - LSE[b,hq,i]),
+ *   s_ij = scale * <q[b,i,hq,:], k[b,j,g,:]>,  LSE = log sum_{allowed j} exp(s_ij),
+ *   g = hq / (h / h_kv), sums over allowed keys only.
+ *
+ *   q   [n,l_q,h,d]     in   dtype
+ *   k,v [n,l_k,h_kv,d]  in   dtype
+ *   out [n,l_q,h,d]     out  dtype (rounded to nearest even)
+ *   lse [n,h,l_q]       out  float32, natural log, -inf for empty rows
+ *   d in {64, 128}; 0 <= scale < inf (the pages use 1/sqrt(d)).
+ * out and lse must not overlap q, k or v.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int n, int l_q, int l_k, int h, int h_kv, int d,
+             float scale, int causal, int win_l, int win_r,
+             long long q_offset, long long k_offset, void* stream, int dtype);
+
+/*
+ * attn_merge - merge a partial result over one key chunk into an accumulator
+ * over other keys (flash_sharding.py ring_fwd, log1p form; picotron
+ * update_out_and_lse, sigmoid form - the two are equal):
+ *   lse = max(a,b) + log1p(exp(min(a,b) - max(a,b)))
+ *   out_acc = out_acc * exp(a - lse) + float(out_blk) * exp(b - lse)
+ * with a = lse_acc, b = lse_blk per row (b, hq, i).  If b = -inf the row is
+ * left unchanged; if a = -inf (and b is not) the row becomes (out_blk, b)
+ * whatever out_acc held before, so an uninitialised accumulator with LSE
+ * -inf is safe.
+ *
+ *   out_acc [n,l,h,d] float32  in/out      lse_acc [n,h,l] float32 in/out
+ *   out_blk [n,l,h,d] blk_dtype in         lse_blk [n,h,l] float32 in
+ *   any d >= 1.  out_blk / lse_blk must not overlap out_acc / lse_acc.
+ */
+int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
+               const float* lse_blk, int n, int l, int h, int d, int blk_dtype,
+               void* stream);
+
+/*
+ * attn_acc_init - set a ring accumulator to the empty result, O = 0 and
+ * LSE = -inf (flash_sharding.py ring_fwd, its initial o and lse).
+ *   out_acc [n,l,h,d] float32 out; lse_acc [n,h,l] float32 out.
+ */
+int attn_acc_init(float* out_acc, float* lse_acc, int n, int l, int h, int d,
+                  void* stream);
+
+/*
+ * attn_acc_cast - final cast of the ring accumulator to the query dtype,
+ * rounding to nearest even (flash_sharding.py ring_fwd, o.astype(q.dtype)).
+ *   out_acc [n,l,h,d] float32 in; out [n,l,h,d] dtype out (may not overlap).
+ */
+int attn_acc_cast(const float* out_acc, void* out, int n, int l, int h, int d,
+                  int dtype, void* stream);
+
+/*
+ * attn_bwd - exact attention backward by recomputation from the saved LSE
+ * (picotron ring_attention_backward; flash_sharding.py bwd argument order
+ * dout, q, k, v, out, lse and gradients in the query dtype):
+ *   P = exp(S - LSE), D_i = sum_c dout_ic out_ic, dP = dout V^T,
+ *   dS = P * (dP - D) (0 where masked), dQ = scale dS K, dK = scale dS^T Q,
+ *   dV = P^T dout; with grouped heads dK and dV of a key/value head sum over
+ *   the query heads that read it.  Accumulation is float32.
+ *
+ *   dout, q, out [n,l_q,h,d] dtype in;  k, v [n,l_k,h_kv,d] dtype in
+ *   lse [n,h,l_q] float32 in (as written by attn_fwd)
+ *   dq [n,l_q,h,d], dk, dv [n,l_k,h_kv,d] dtype out
+ *   workspace: device scratch of at least attn_bwd_workspace_bytes(...) bytes,
+ *   owned by the caller; its contents on entry do not matter.
+ * Outputs must not overlap inputs, the workspace or each other.
+ */
+int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
+             const void* out, const float* lse, void* dq, void* dk, void* dv,
+             int n, int l_q, int l_k, int h, int h_kv, int d,
+             float scale, int causal, int win_l, int win_r,
+             long long q_offset, long long k_offset,
+             void* workspace, size_t workspace_bytes, void* stream, int dtype);
+
+/* Bytes of workspace attn_bwd needs for these sizes (0 on invalid sizes). */
+size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKWISE_EXACT_ATTENTION_AMD_ATTN_H */

@@ -1,0 +1,165 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, and rejects bad arguments before making
+any HIP call.  Pointers here are fake addresses: each call must fail its
+argument checks, so nothing is ever dereferenced or launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from blockwise_exact_attention_amd import _lib
+from blockwise_exact_attention_amd._lib import (
+    ATTN_BF16, ATTN_ERR_ALIAS, ATTN_ERR_ALIGN, ATTN_ERR_NULL, ATTN_ERR_SHAPE,
+    ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_F32, ATTN_OK)
+from blockwise_exact_attention_amd.flops import allowed_pairs
+import oracle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "attn.h")
+
+A = 1 << 32          # fake, well-aligned, far-apart device addresses
+B = 2 << 32
+C = 3 << 32
+D_ = 4 << 32
+E = 5 << 32
+F = 6 << 32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_merge", "attn_bwd", "attn_acc_init",
+              "attn_acc_cast", "attn_bwd_workspace_bytes",
+              "attn_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings():
+    for s in range(8):
+        assert _lib.status_string(s)
+    assert _lib.status_string(ATTN_OK) == "ok"
+
+
+def _fwd(**kw):
+    a = dict(q=A, k=B, v=C, out=D_, lse=E, n=1, l_q=128, l_k=128, h=2, h_kv=2,
+             d=64, scale=0.125, causal=0, win_l=-1, win_r=-1, q_offset=0,
+             k_offset=0, stream=None, dtype=ATTN_BF16)
+    a.update(kw)
+    return _lib.lib().attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"],
+                               a["n"], a["l_q"], a["l_k"], a["h"], a["h_kv"],
+                               a["d"], a["scale"], a["causal"], a["win_l"],
+                               a["win_r"], a["q_offset"], a["k_offset"],
+                               a["stream"], a["dtype"])
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "out", "lse"])
+def test_fwd_null(field):
+    assert _fwd(**{field: None}) == ATTN_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(n=0), dict(l_q=0), dict(l_k=-1),
+                                dict(h=0), dict(h_kv=0), dict(h=6, h_kv=4),
+                                dict(d=0), dict(n=1 << 30, l_q=1 << 30)])
+def test_fwd_shape(kw):
+    assert _fwd(**kw) == ATTN_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=256), dict(dtype=7),
+                                dict(scale=float("inf")),
+                                dict(scale=float("nan"))])
+def test_fwd_unsupported(kw):
+    assert _fwd(**kw) == ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(q=A + 2), dict(out=D_ + 8),
+                                dict(lse=E + 2)])
+def test_fwd_align(kw):
+    assert _fwd(**kw) == ATTN_ERR_ALIGN
+
+
+@pytest.mark.parametrize("kw", [dict(out=A), dict(out=A + 64), dict(lse=C + 16),
+                                dict(lse=D_ + 32)])
+def test_fwd_alias(kw):
+    assert _fwd(**kw) == ATTN_ERR_ALIAS
+
+
+def test_merge_checks():
+    L = _lib.lib()
+    ok = dict(a=A, la=B, b=C, lb=D_, n=1, l=16, h=2, d=64, dt=ATTN_BF16)
+
+    def call(**kw):
+        x = dict(ok)
+        x.update(kw)
+        return L.attn_merge(x["a"], x["la"], x["b"], x["lb"], x["n"], x["l"],
+                            x["h"], x["d"], x["dt"], None)
+    assert call(a=None) == ATTN_ERR_NULL
+    assert call(lb=None) == ATTN_ERR_NULL
+    assert call(l=0) == ATTN_ERR_SHAPE
+    assert call(dt=3) == ATTN_ERR_UNSUPPORTED
+    assert call(a=A + 4) == ATTN_ERR_ALIGN
+    assert call(b=A + 16) == ATTN_ERR_ALIAS
+    assert call(lb=B) == ATTN_ERR_ALIAS
+    assert L.attn_acc_init(None, B, 1, 2, 3, 4, None) == ATTN_ERR_NULL
+    assert L.attn_acc_init(A, A + 8, 1, 2, 3, 4, None) == ATTN_ERR_ALIAS
+    assert L.attn_acc_cast(A, B, 1, 2, 3, 4, 9, None) == ATTN_ERR_UNSUPPORTED
+    assert L.attn_acc_cast(A, A + 16, 1, 2, 3, 4, ATTN_F32, None) == ATTN_ERR_ALIAS
+
+
+def test_bwd_checks():
+    L = _lib.lib()
+    need = L.attn_bwd_workspace_bytes(1, 128, 128, 2, 2, 64)
+    assert need > 0
+    assert L.attn_bwd_workspace_bytes(1, 128, 128, 3, 2, 64) == 0
+
+    ptrs = [A, A + (1 << 28), B, B + (1 << 28), C, C + (1 << 28), D_,
+            D_ + (1 << 28), E]
+
+    def call(ptrs=ptrs, ws=F, wsb=need, d=64, h=2, h_kv=2, dtype=ATTN_BF16):
+        return L.attn_bwd(*ptrs, 1, 128, 128, h, h_kv, d, 0.125, 1, -1, -1, 0,
+                          0, ws, wsb, None, dtype)
+    bad = list(ptrs)
+    bad[3] = None
+    assert call(ptrs=bad) == ATTN_ERR_NULL
+    assert call(h=3) == ATTN_ERR_SHAPE
+    assert call(d=32) == ATTN_ERR_UNSUPPORTED
+    assert call(ws=None) == ATTN_ERR_WORKSPACE
+    assert call(wsb=need - 1) == ATTN_ERR_WORKSPACE
+    alias = list(ptrs)
+    alias[6] = ptrs[1]          # dq on top of q
+    assert call(ptrs=alias) == ATTN_ERR_ALIAS
+    assert call(ws=ptrs[7]) == ATTN_ERR_ALIAS   # workspace on top of dk
+
+
+def test_allowed_pairs_matches_oracle_mask():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        l_q = int(rng.integers(1, 40))
+        l_k = int(rng.integers(1, 40))
+        causal = bool(rng.integers(0, 2))
+        wl = int(rng.integers(-1, 8))
+        wr = int(rng.integers(-1, 8))
+        qo = int(rng.integers(-20, 20))
+        ko = int(rng.integers(-20, 20))
+        m = oracle.allowed_mask(np.arange(l_q), np.arange(l_k), causal, wl, wr,
+                                qo, ko)
+        assert allowed_pairs(l_q, l_k, causal, wl, wr, qo, ko) == int(m.sum())
+    # the workloads' pair counts
+    assert allowed_pairs(2048, 2048, True) == 2098176
+    assert allowed_pairs(4096, 4096, True, 256, 0) == 1019776
+    assert allowed_pairs(1024, 1024, True, -1, -1, 7168, 7168) == 524800
+    assert allowed_pairs(16384, 16384, True) == 134225920

@@ -1,0 +1,249 @@
+"""GPU parity of the forward pass, the merge and the ring share against the
+fp64 oracle, through the C ABI (blockwise_exact_attention_amd.attention).
+
+Sizes: the five workloads at their full shapes (the oracle computes every
+output where that takes seconds, and sampled heads or rows otherwise), plus
+small cases that span several tiles, ragged tails, every mask mode, grouped
+and multi-query heads and the degenerate cases (one key, one query, empty
+rows, zero and negative scale)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from blockwise_exact_attention_amd import attention as A
+from blockwise_exact_attention_amd.inputs import draw_normal, round_to_bf16
+from blockwise_exact_attention_amd.workloads import WORKLOADS, make_inputs
+from gpu_util import check_o_lse, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(q, k, v, dtype, scale, causal=False, wl=-1, wr=-1, qo=0, ko=0):
+    tq, tk, tv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    o, lse = A.attention_forward(tq, tk, tv, scale, causal, (wl, wr), qo, ko)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+def rand_inputs(seed, n, l_q, l_k, h, h_kv, d, dtype):
+    q, k, v = draw_normal(seed, [(n, l_q, h, d), (n, l_k, h_kv, d),
+                                 (n, l_k, h_kv, d)])
+    if dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return q, k, v
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_c1_tiny_fp32():
+    w = WORKLOADS["C1"]
+    say(f"[C1] {w}")
+    x = make_inputs(w)
+    o, lse = run_fwd(x["q"], x["k"], x["v"], "f32", w.softmax_scale, w.causal)
+    ro, rl = oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale,
+                                  w.causal)
+    check_o_lse(o, lse, ro, rl, "f32", "C1")
+
+
+def test_c2_causal_mha_full():
+    w = WORKLOADS["C2"]
+    say(f"[C2] {w}")
+    x = make_inputs(w)
+    o, lse = run_fwd(x["q"], x["k"], x["v"], "bf16", w.softmax_scale, True)
+    ro, rl = oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale, True)
+    check_o_lse(o, lse, ro, rl, "bf16", "C2")
+
+
+def test_c3_ring_share():
+    """Rank 7 of 8: the merged share equals rows 7168..8191 of causal
+    attention over the full 8192-token sequence (sampled heads, one from
+    each key/value group and both ends of a group)."""
+    w = WORKLOADS["C3"]
+    say(f"[C3] {w}")
+    x = make_inputs(w)
+    tq = dev(x["q"], "bf16")
+    kc = [dev(c, "bf16") for c in x["k_chunks"]]
+    vc = [dev(c, "bf16") for c in x["v_chunks"]]
+    share = A.RingShare(tq, w.softmax_scale, True, x["q_offset"])
+    out, lse_acc = share.run(kc, vc, x["k_offsets"])
+    torch.cuda.synchronize()
+    o, lse = host(out), host(lse_acc)
+    heads = [(0, 0), (0, 3), (0, 6), (0, 13), (0, 21), (0, 31)]
+    q_full_rows = x["q"]
+    ro, rl = oracle.attention_fwd(q_full_rows, x["k_full"], x["v_full"],
+                                  w.softmax_scale, True, -1, -1,
+                                  x["q_offset"], 0, heads=heads)
+    check_o_lse(o, lse, ro, rl, "bf16", "C3 ring share vs full-sequence rows")
+    # the single steps too: step 0 (wholly in the past) and step 7 (diagonal)
+    for s in (0, 7):
+        ob, lb = run_fwd(x["q"], x["k_chunks"][s], x["v_chunks"][s], "bf16",
+                         w.softmax_scale, True, -1, -1, x["q_offset"],
+                         x["k_offsets"][s])
+        rob, rlb = oracle.attention_fwd(x["q"], x["k_chunks"][s],
+                                        x["v_chunks"][s], w.softmax_scale,
+                                        True, -1, -1, x["q_offset"],
+                                        x["k_offsets"][s], heads=heads)
+        check_o_lse(ob, lb, rob, rlb, "bf16", f"C3 step {s}")
+
+
+def test_c4_sliding_window_full():
+    w = WORKLOADS["C4"]
+    say(f"[C4] {w}")
+    x = make_inputs(w)
+    o, lse = run_fwd(x["q"], x["k"], x["v"], "bf16", w.softmax_scale, True,
+                     w.win_l, w.win_r)
+    ro, rl = oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale,
+                                  True, w.win_l, w.win_r, block=256)
+    check_o_lse(o, lse, ro, rl, "bf16", "C4")
+
+
+def test_c5_forward_sampled_rows():
+    w = WORKLOADS["C5"]
+    say(f"[C5 fwd] {w}")
+    x = make_inputs(w)
+    o, lse = run_fwd(x["q"], x["k"], x["v"], "bf16", w.softmax_scale, True)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([
+        [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, 8191, 8192, 16383],
+        rng.integers(0, w.l_q, 200)]))
+    heads = [(0, 0), (0, 7), (0, 15)]
+    ro, rl = oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale,
+                                  True, heads=heads, rows=rows)
+    check_o_lse(o, lse, ro, rl, "bf16", "C5 forward (sampled rows)")
+
+
+# ---------------------------------------------------------------- small cases
+
+SMALL = [
+    # n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko
+    (1, 200, 333, 4, 2, 128, False, -1, -1, 0, 0),
+    (2, 300, 300, 4, 4, 64, True, -1, -1, 0, 0),
+    (1, 257, 513, 8, 2, 128, True, -1, -1, 256, 0),     # bottom-right-ish
+    (1, 130, 700, 3, 1, 64, True, 40, 7, 100, 0),       # MQA + window
+    (2, 256, 256, 2, 2, 128, True, 0, 0, 0, 0),         # diagonal only
+    (1, 190, 190, 2, 1, 128, False, 31, 31, 0, 0),
+    (1, 96, 160, 4, 4, 64, True, -1, -1, 0, 64),        # rows 0..63 empty
+    (1, 64, 64, 2, 2, 128, True, -1, -1, 0, 1000),      # every row empty
+    (1, 1, 1, 1, 1, 64, False, -1, -1, 0, 0),
+    (1, 1, 300, 2, 1, 128, True, -1, -1, 299, 0),       # single query, last
+    (1, 300, 1, 2, 2, 64, False, -1, -1, 0, 0),         # single key
+    (2, 129, 129, 8, 1, 64, False, -1, 5, 0, 0),        # right window only
+    (1, 512, 512, 16, 8, 128, True, -1, -1, 0, 0),      # n*h_kv % 8 == 0 path
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", SMALL)
+def test_small_cases(case, dtype):
+    n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko = case
+    say(f"[small] {case} {dtype}")
+    q, k, v = rand_inputs(7 + l_q + l_k + h + d, n, l_q, l_k, h, h_kv, d, dtype)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_fwd(q, k, v, dtype, scale, causal, wl, wr, qo, ko)
+    ro, rl = oracle.attention_fwd(q, k, v, scale, causal, wl, wr, qo, ko)
+    check_o_lse(o, lse, ro, rl, dtype, str(case))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.4])
+def test_scale_values(scale, dtype):
+    q, k, v = rand_inputs(99, 1, 160, 200, 2, 2, 128, dtype)
+    o, lse = run_fwd(q, k, v, dtype, scale, True, -1, -1, 40, 0)
+    ro, rl = oracle.attention_fwd(q, k, v, scale, True, -1, -1, 40, 0)
+    check_o_lse(o, lse, ro, rl, dtype, f"scale={scale}")
+
+
+def test_forward_is_deterministic():
+    q, k, v = rand_inputs(3, 1, 1024, 1024, 8, 2, 128, "bf16")
+    tq, tk, tv = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    o1, l1 = A.attention_forward(tq, tk, tv, 0.088, True)
+    o2, l2 = A.attention_forward(tq, tk, tv, 0.088, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_large_offsets():
+    q, k, v = rand_inputs(4, 1, 100, 100, 2, 2, 64, "bf16")
+    for qo, ko in [(2**40 + 50, 2**40), (-(2**50), -(2**50) + 30),
+                   (2**62, -(2**62)), (-(2**62), 2**62)]:
+        o, lse = run_fwd(q, k, v, "bf16", 0.125, True, -1, -1, qo, ko)
+        dq = max(min(qo - ko, 10**6), -10**6)
+        ro, rl = oracle.attention_fwd(q, k, v, 0.125, True, -1, -1, dq, 0)
+        check_o_lse(o, lse, ro, rl, "bf16", f"offsets {qo},{ko}")
+
+
+# ---------------------------------------------------------------- merge
+
+def _partial(rng, n, l, h, d, p_empty):
+    o = rng.standard_normal((n, l, h, d)).astype(np.float32)
+    lse = (rng.standard_normal((n, h, l)) * 4).astype(np.float32)
+    empty = rng.random((n, h, l)) < p_empty
+    lse[empty] = -np.inf
+    o[np.transpose(empty, (0, 2, 1))] = 0.0
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [128, 64, 5])
+@pytest.mark.parametrize("blk_dtype", ["bf16", "f32"])
+def test_merge_parity(d, blk_dtype):
+    rng = np.random.default_rng(d)
+    n, l, h = 2, 77, 3
+    oa, la = _partial(rng, n, l, h, d, 0.2)
+    ob, lb = _partial(rng, n, l, h, d, 0.2)
+    if blk_dtype == "bf16":
+        ob = round_to_bf16(ob)
+    acc = torch.from_numpy(oa).cuda()
+    lacc = torch.from_numpy(la).cuda()
+    # an accumulator row with LSE -inf must be overwritten, whatever it holds
+    acc_np_nan = oa.copy()
+    acc_np_nan[np.transpose(np.isneginf(la), (0, 2, 1))] = np.nan
+    acc.copy_(torch.from_numpy(acc_np_nan))
+    A.attn_merge(acc, lacc, dev(ob, blk_dtype),
+                 torch.from_numpy(lb).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge(oa, la, ob, lb)
+    go, gl = host(acc), host(lacc)
+    both = np.transpose(np.isneginf(la) & np.isneginf(lb), (0, 2, 1))
+    keep = ~np.broadcast_to(both[..., None], go.shape)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.max(np.abs(gl[fin] - rl[fin])) < 2e-6
+    assert np.max(np.abs(go[keep] - ro[keep])) < 2e-5
+
+
+def test_acc_init_and_cast():
+    n, l, h, d = 1, 33, 3, 64
+    acc = torch.full((n, l, h, d), 7.0, device="cuda")
+    lse = torch.zeros((n, h, l), device="cuda")
+    A.attn_acc_init(acc, lse)
+    torch.cuda.synchronize()
+    assert torch.all(acc == 0) and torch.all(torch.isneginf(lse))
+    x = torch.randn((n, l, h, d), device="cuda") * 3
+    out = torch.empty((n, l, h, d), dtype=torch.bfloat16, device="cuda")
+    A.attn_acc_cast(x, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), x.cpu().to(torch.bfloat16))
+    out32 = torch.empty((n, l, h, d), dtype=torch.float32, device="cuda")
+    A.attn_acc_cast(x, out32)
+    torch.cuda.synchronize()
+    assert torch.equal(out32, x)
+
+
+def test_small_ring_share_gqa():
+    """A small ring (P = 4 chunks of 96) on every rank, against causal
+    attention over the whole sequence."""
+    P, c, h, h_kv, d = 4, 96, 8, 2, 128
+    q, k, v = rand_inputs(21, 1, P * c, P * c, h, h_kv, d, "bf16")
+    ro, rl = oracle.attention_fwd(q, k, v, 0.1, True)
+    kc = [dev(k[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
+    vc = [dev(v[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
+    for r in range(P):
+        tq = dev(q[:, r * c:(r + 1) * c], "bf16")
+        out, lse = A.ring_share(tq, kc, vc, [s * c for s in range(P)], r * c,
+                                0.1, True)
+        torch.cuda.synchronize()
+        check_o_lse(host(out), host(lse), ro[:, r * c:(r + 1) * c],
+                    rl[:, :, r * c:(r + 1) * c], "bf16", f"ring rank {r}")
