@@ -184,6 +184,7 @@ int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
     return ATTN_ERR_NULL;
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   const size_t need = bea::bwd_workspace_bytes(n, l_q, h);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) ||

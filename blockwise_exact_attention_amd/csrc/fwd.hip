@@ -75,7 +75,7 @@ __device__ __forceinline__ void map_block(const FwdParams& p, int& tile,
 }
 
 template <int D, int BN>
-struct FwdSmem {
+struct __attribute__((aligned(16))) FwdSmem {
   static constexpr int kKStride = D + 8;   // bf16 per K row (16 B pad)
   static constexpr int kVStride = BN + 8;  // bf16 per V^T row (16 B pad)
   uint16_t k[BN * kKStride];

@@ -63,8 +63,8 @@ enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL                        */
   ATTN_ERR_SHAPE = 2,       /* a size is <= 0, h % h_kv != 0, or sizes overflow  */
-  ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite or
-                               negative scale                                    */
+  ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite
+                               scale, or fp32 backward                           */
   ATTN_ERR_HIP = 4,         /* the HIP runtime reported a launch failure         */
   ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
   ATTN_ERR_ALIAS = 6,       /* an input buffer overlaps an output buffer         */
@@ -87,7 +87,7 @@ enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
  *   k,v [n,l_k,h_kv,d]  in   dtype
  *   out [n,l_q,h,d]     out  dtype (rounded to nearest even)
  *   lse [n,h,l_q]       out  float32, natural log, -inf for empty rows
- *   d in {64, 128}; 0 <= scale < inf (the pages use 1/sqrt(d)).
+ *   d in {64, 128}; any finite scale (the pages use 1/sqrt(d)).
  * out and lse must not overlap q, k or v.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -139,6 +139,7 @@ int attn_acc_cast(const float* out_acc, void* out, int n, int l, int h, int d,
  *   dV = P^T dout; with grouped heads dK and dV of a key/value head sum over
  *   the query heads that read it.  Accumulation is float32.
  *
+ *   dtype must be ATTN_BF16 (ATTN_F32 returns ATTN_ERR_UNSUPPORTED).
  *   dout, q, out [n,l_q,h,d] dtype in;  k, v [n,l_k,h_kv,d] dtype in
  *   lse [n,h,l_q] float32 in (as written by attn_fwd)
  *   dq [n,l_q,h,d], dk, dv [n,l_k,h_kv,d] dtype out

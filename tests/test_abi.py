@@ -137,6 +137,7 @@ def test_bwd_checks():
     assert call(ptrs=bad) == ATTN_ERR_NULL
     assert call(h=3) == ATTN_ERR_SHAPE
     assert call(d=32) == ATTN_ERR_UNSUPPORTED
+    assert call(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
     assert call(ws=None) == ATTN_ERR_WORKSPACE
     assert call(wsb=need - 1) == ATTN_ERR_WORKSPACE
     alias = list(ptrs)

@@ -1,0 +1,124 @@
+"""GPU parity of the backward pass (dQ, dK, dV) against the fp64 oracle,
+through the C ABI.  The GPU backward consumes the GPU forward's bf16 O and
+fp32 LSE, as the ring backward on the pages does with the saved out and
+softmax_lse; the oracle recomputes everything in fp64 from q, k, v and dO.
+
+Tolerance (the pages give none for gradients): max |g - g_ref| <=
+2e-2 * max(1, max |g_ref|) per gradient, the forward's bf16 bound scaled to
+the gradient's magnitude; the relative Frobenius error is printed too."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from blockwise_exact_attention_amd import attention as A
+from blockwise_exact_attention_amd.inputs import draw_normal, round_to_bf16
+from blockwise_exact_attention_amd.workloads import WORKLOADS, make_inputs
+from gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def check_grad(g, ref, name):
+    sel = ~np.isnan(ref)
+    assert np.all(np.isfinite(g[sel])), f"{name}: non-finite"
+    scale = max(1.0, float(np.max(np.abs(ref[sel]), initial=0.0)))
+    err = float(np.max(np.abs(g[sel] - ref[sel]), initial=0.0))
+    fro = float(np.linalg.norm(g[sel] - ref[sel]) /
+                max(np.linalg.norm(ref[sel]), 1e-30))
+    say(f"  {name}: max|err| = {err:.3e} (tol {2e-2 * scale:.3e}), "
+        f"rel fro = {fro:.3e}")
+    assert err <= 2e-2 * scale, f"{name}: {err} > {2e-2 * scale}"
+    return err
+
+
+def run_fwd_bwd(q, k, v, do, scale, causal, wl=-1, wr=-1, qo=0, ko=0):
+    tq, tk, tv, tdo = (dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = A.attention_forward(tq, tk, tv, scale, causal, (wl, wr), qo, ko)
+    dq, dk, dv = A.attention_backward(tdo, tq, tk, tv, o, lse, scale, causal,
+                                      (wl, wr), qo, ko)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv)
+
+
+CASES = [
+    # n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko
+    (1, 256, 256, 2, 2, 128, True, -1, -1, 0, 0),
+    (2, 200, 333, 4, 2, 128, False, -1, -1, 0, 0),
+    (1, 300, 300, 4, 4, 64, True, -1, -1, 0, 0),
+    (1, 257, 513, 8, 2, 128, True, -1, -1, 256, 0),
+    (1, 130, 700, 3, 1, 64, True, 40, 7, 100, 0),
+    (1, 96, 160, 4, 4, 64, True, -1, -1, 0, 64),       # empty rows
+    (1, 64, 64, 2, 2, 128, True, -1, -1, 0, 1000),     # every row empty
+    (1, 1, 300, 2, 1, 128, True, -1, -1, 299, 0),
+    (1, 300, 1, 2, 2, 64, False, -1, -1, 0, 0),
+    (2, 129, 129, 8, 1, 64, False, -1, 5, 0, 0),
+    (1, 512, 384, 8, 2, 128, True, 100, 0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_backward_small(case):
+    n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko = case
+    say(f"[bwd] {case}")
+    q, k, v, do = draw_normal(11 + l_q + l_k + h, [(n, l_q, h, d),
+                                                  (n, l_k, h_kv, d),
+                                                  (n, l_k, h_kv, d),
+                                                  (n, l_q, h, d)])
+    q, k, v, do = (round_to_bf16(x) for x in (q, k, v, do))
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = run_fwd_bwd(q, k, v, do, scale, causal, wl, wr, qo, ko)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, scale, causal, wl, wr, qo,
+                                      ko)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
+def test_backward_negative_scale():
+    q, k, v, do = draw_normal(5, [(1, 200, 2, 128), (1, 200, 1, 128),
+                                  (1, 200, 1, 128), (1, 200, 2, 128)])
+    q, k, v, do = (round_to_bf16(x) for x in (q, k, v, do))
+    dq, dk, dv = run_fwd_bwd(q, k, v, do, -0.07, True)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, -0.07, True)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
+def test_backward_is_deterministic():
+    q, k, v, do = draw_normal(6, [(1, 512, 4, 128), (1, 512, 2, 128),
+                                  (1, 512, 2, 128), (1, 512, 4, 128)])
+    tq, tk, tv, tdo = (dev(round_to_bf16(x), "bf16") for x in (q, k, v, do))
+    o, lse = A.attention_forward(tq, tk, tv, 0.088, True)
+    a = A.attention_backward(tdo, tq, tk, tv, o, lse, 0.088, True)
+    b = A.attention_backward(tdo, tq, tk, tv, o, lse, 0.088, True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_c5_backward_sampled_heads():
+    """Long-context workload at full size (l = 16384, 16 heads); the oracle
+    computes the complete gradients of two whole heads."""
+    w = WORKLOADS["C5"]
+    say(f"[C5 bwd] {w}")
+    x = make_inputs(w)
+    dq, dk, dv = run_fwd_bwd(x["q"], x["k"], x["v"], x["do"], w.softmax_scale,
+                             True)
+    heads = [(0, 0), (0, 9)]
+    rq, rk, rv = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"],
+                                      w.softmax_scale, True, kv_heads=heads,
+                                      block=1024)
+    check_grad(dq, rq, "C5 dq")
+    check_grad(dk, rk, "C5 dk")
+    check_grad(dv, rv, "C5 dv")
+
+
+def test_fp32_backward_is_rejected():
+    q = torch.zeros((1, 64, 2, 64), device="cuda")
+    lse = torch.zeros((1, 2, 64), device="cuda")
+    with pytest.raises(A.AttnError if hasattr(A, "AttnError") else Exception):
+        A.attention_backward(q, q, q, q, q, lse)
