@@ -43,7 +43,8 @@ struct FwdParams {
   int n_qtiles;
   int xcd_groups;  // 1: keep the workgroups of one key/value head on one XCD
   int reverse;     // 1: launch the last (longest, under causal) q tiles first
-  float c;         // scale * log2(e)
+  float c;         // |scale| * log2(e)
+  int neg_scale;   // 1: scale < 0 (Q enters with flipped sign)
   int dlo, dhi;
 };
 
@@ -78,8 +79,8 @@ template <int D, int BN>
 struct __attribute__((aligned(16))) FwdSmem {
   static constexpr int kKStride = D + 8;   // bf16 per K row (16 B pad)
   static constexpr int kVStride = BN + 8;  // bf16 per V^T row (16 B pad)
-  uint16_t k[BN * kKStride];
-  uint16_t vt[D * kVStride];
+  uint16_t k[2][BN * kKStride];            // double-buffered K tiles
+  uint16_t vt[2][D * kVStride];            // double-buffered V^T tiles
 };
 
 // Position of key kk (0..BN-1) inside a V^T row: within each group of 16 keys
@@ -89,10 +90,32 @@ __device__ __forceinline__ int vt_pos(int kk) {
   return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
 }
 
-template <int D, int BN, bool NEGS>
+// The other half-wave's copy of x (lane l <-> lane l ^ 32), then combined:
+// v_permlane32_swap hands lanes 0-31 the upper half's value in its second
+// result and lanes 32-63 the lower half's value in its first result, so
+// max/sum of the two results is the max/sum over the pair on every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Growth of the running row max (log2 units) that forces a rescale of the
+// accumulators.  Below it the stale max is kept: exponentials are then at most
+// 2^8, exact in meaning (O = sum p v / sum p for any fixed shift) and far from
+// fp32 or bf16 range limits.
+constexpr float kRescaleSlack = 8.f;
+
+template <int D, int BN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
-  static_assert(BN * D / 32 == kThreads, "one V group of 4 keys x 8 dims per thread");
+  static_assert(BN * D / 32 <= kThreads, "at most one V group of 4 keys x 8 dims per thread");
   static_assert((BN * D / 8) % kThreads == 0, "whole K chunks per thread");
+  constexpr int VGROUPS = BN * D / 32;
   constexpr int KS = FwdSmem<D, BN>::kKStride;
   constexpr int VS = FwdSmem<D, BN>::kVStride;
   constexpr int KCH = BN * D / 8 / kThreads;
@@ -136,34 +159,41 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const long long wjlo = max(0LL, (long long)wa + p.dlo);
   const long long wjhi = min((long long)p.l_k - 1, (long long)wb + p.dhi);
 
-  // Q fragment: B operand of S^T = K Q^T, resident for the whole loop.
+  // Q fragment: B operand of S^T = K Q^T, resident for the whole loop.  A
+  // negative scale is folded into Q by flipping its sign bits (exact), so the
+  // scores and c = |scale| log2(e) keep the positive-scale code path.
   const size_t q_row = (size_t)p.h * D;
   const uint16_t* qptr = p.q + ((size_t)b * p.l_q + min(qi, last_row)) * q_row +
                          (size_t)hq * D + 8 * half;
+  const uint32_t qsign = p.neg_scale ? 0x80008000u : 0u;
   u32x4_t qf[NDS];
 #pragma unroll
   for (int s = 0; s < NDS; ++s)
-    qf[s] = *reinterpret_cast<const u32x4_t*>(qptr + 16 * s);
+    qf[s] = *reinterpret_cast<const u32x4_t*>(qptr + 16 * s) ^ qsign;
 
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m = kNegInf;  // running row max in log2 units (scale*log2e*s)
+  float m = kNegInf;  // row max used for the exponentials (log2 units)
   float lsum = 0.f;   // this lane's half of the running row sum
 
   const size_t kv_row = (size_t)p.h_kv * D;
   const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
   const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
 
-  // Register staging of the next tile (global -> VGPR -> LDS).
+  // Register staging (global -> VGPR -> LDS).  K: 16-byte chunks, 16 threads
+  // per row.  V: each thread owns 4 consecutive keys x 8 dims; the 16 (or 32)
+  // threads of one dim chunk cover consecutive key groups, so the transposed
+  // 8-byte LDS writes of a half-wave land on one contiguous V^T row segment.
   u32x4_t kreg[KCH];
   u32x4_t vreg[4];
-  const int vg_key = (tid / (D / 8)) * 4;  // first of this thread's 4 V keys
-  const int vg_c8 = tid % (D / 8);         // its 8-dim chunk
+  const int v_kg = tid % (BN / 4);
+  const int v_c8 = tid / (BN / 4);
+  const int v_pos = vt_pos(4 * v_kg);
 
-  auto gload = [&](int kt) {
+  auto load_k = [&](int kt) {
     const int j0 = kt * BN;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
@@ -173,132 +203,160 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       const int j = min(j0 + row, p.l_k - 1);
       kreg[c] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)j * kv_row + c8 * 8);
     }
+  };
+  const bool v_owner = VGROUPS == kThreads || tid < VGROUPS;
+  auto load_v = [&](int kt) {
+    if (!v_owner) return;
+    const int j0 = kt * BN + 4 * v_kg;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = min(j0 + vg_key + r, p.l_k - 1);
-      vreg[r] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)j * kv_row + vg_c8 * 8);
+      const int j = min(j0 + r, p.l_k - 1);
+      vreg[r] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)j * kv_row + v_c8 * 8);
     }
   };
-  auto sstore = [&]() {
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int id = tid + c * kThreads;
       const int row = id / (D / 8);
       const int c8 = id % (D / 8);
-      *reinterpret_cast<u32x4_t*>(&sm.k[row * KS + c8 * 8]) = kreg[c];
+      *reinterpret_cast<u32x4_t*>(&sm.k[buf][row * KS + c8 * 8]) = kreg[c];
     }
-    const int pos = vt_pos(vg_key);
+  };
+  auto store_v = [&](int buf) {
+    if (!v_owner) return;
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       const int w = dd >> 1;
       const int sh = (dd & 1) * 16;
-      const uint32_t e0 = (vreg[0][w] >> sh) & 0xffffu;
-      const uint32_t e1 = (vreg[1][w] >> sh) & 0xffffu;
-      const uint32_t e2 = (vreg[2][w] >> sh) & 0xffffu;
-      const uint32_t e3 = (vreg[3][w] >> sh) & 0xffffu;
       u32x2_t pk;
-      pk[0] = e0 | (e1 << 16);
-      pk[1] = e2 | (e3 << 16);
-      *reinterpret_cast<u32x2_t*>(&sm.vt[(vg_c8 * 8 + dd) * VS + pos]) = pk;
+      pk[0] = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
+      pk[1] = ((vreg[2][w] >> sh) & 0xffffu) | (((vreg[3][w] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<u32x2_t*>(&sm.vt[buf][(v_c8 * 8 + dd) * VS + v_pos]) = pk;
     }
   };
-
-  if (kt_begin < kt_end) {
-    gload(kt_begin);
-    sstore();
-  }
-
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    __syncthreads();
-    if (kt + 1 < kt_end) gload(kt + 1);
+  auto live = [&](int kt) {
+    const long long j0 = (long long)kt * BN;
+    return wave_live && j0 <= wjhi && j0 + BN - 1 >= wjlo;
+  };
+  // S^T = K Q^T for one tile: NKB blocks of 32 keys x 32 queries.
+  auto scores = [&](int kt, f32x16_t (&sacc)[NKB]) {
+    const uint16_t* kl = sm.k[kt & 1];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+            &kl[(32 * kb + col) * KS + 16 * s + 8 * half]);
+        sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
+      }
+    }
+  };
+  // Online-softmax update with the tile's scores, then O^T += V^T P^T.
+  auto softmax_pv = [&](int kt, f32x16_t (&sacc)[NKB]) {
     const int j0 = kt * BN;
-    const bool live = wave_live && (long long)j0 <= wjhi &&
-                      (long long)(j0 + BN - 1) >= wjlo;
-    if (live) {
-      const bool full = (j0 + BN <= p.l_k) &&
-                        ((long long)j0 - wb >= p.dlo) &&
-                        ((long long)(j0 + BN - 1) - wa <= p.dhi);
-      // ---- S^T = K Q^T for the tile: NKB blocks of 32 keys x 32 queries
-      f32x16_t sacc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < NDS; ++s) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              &sm.k[(32 * kb + col) * KS + 16 * s + 8 * half]);
-          sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
-        }
-      }
-      if (NEGS) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] = -sacc[kb][r];
-      }
-      // ---- mask (boundary tiles only) and row max
-      float mx = kNegInf;
-      if (full) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const int rel = j - qi;
-            const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
-            sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
-            mx = fmaxf(mx, sacc[kb][r]);
-          }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = (mx == kNegInf) ? kNegInf : mx * p.c;
-      const float mnew = fmaxf(m, mt);
-      const float muse = (mnew == kNegInf) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m - muse);
-      m = mnew;
-      // ---- P = exp2(c*s - m) packed to bf16 as the B operand of O^T += V^T P^T
-      u32x4_t pf[NPS];
-      float rs = 0.f;
+    const bool full = (j0 + BN <= p.l_k) && ((long long)j0 - wb >= p.dlo) &&
+                      ((long long)(j0 + BN - 1) - wa <= p.dhi);
+    float mx = kNegInf;
+    if (full) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, -muse));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.c, -muse));
-          if (!full) {
-            p0 = (sacc[kb][r] == kNegInf) ? 0.f : p0;
-            p1 = (sacc[kb][r + 1] == kNegInf) ? 0.f : p1;
-          }
-          rs += p0 + p1;
-          pf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int rel = j - qi;
+          const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
+          sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+          mx = fmaxf(mx, sacc[kb][r]);
         }
-      lsum = lsum * alpha + rs;
+    }
+    mx = pair_max(mx);
+    const float mt = (mx == kNegInf) ? kNegInf : mx * p.c;
+    // keep the stale max unless this tile's max exceeds it by the slack
+    const bool grow = mt > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      // lanes that keep their max keep alpha = 1 (their m may still be -inf,
+      // and -inf - -inf must not reach the exponential)
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;  // m = -inf -> 0
+      m = grow ? mt : m;
+      lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      // ---- O^T += V^T P^T
+    }
+    const float muse = (m == kNegInf) ? 0.f : m;
+    u32x4_t pf[NPS];
+    float rs = 0.f;
 #pragma unroll
-      for (int t = 0; t < NPS; ++t)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              &sm.vt[(32 * db + col) * VS + 16 * t + 8 * half]);
-          oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, -muse));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.c, -muse));
+        if (!full) {
+          p0 = (sacc[kb][r] == kNegInf) ? 0.f : p0;
+          p1 = (sacc[kb][r + 1] == kNegInf) ? 0.f : p1;
         }
+        rs += p0 + p1;
+        pf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+    lsum += rs;
+    const uint16_t* vl = sm.vt[kt & 1];
+#pragma unroll
+    for (int t = 0; t < NPS; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+            &vl[(32 * db + col) * VS + 16 * t + 8 * half]);
+        oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
+      }
+  };
+
+  // Pipeline: while the softmax of tile t runs, the S^T MFMAs of tile t+1 are
+  // already issued; the loads of K(t+2) and V(t+1) are in flight.  K(t+2)
+  // reuses the buffer K(t) had (its scores were taken one step earlier) and
+  // V(t+1) the buffer of V(t-1), so one barrier per tile suffices.
+  f32x16_t sa[NKB], sb[NKB];
+  auto step = [&](int kt, f32x16_t (&cur)[NKB], f32x16_t (&nxt)[NKB]) {
+    const bool has1 = kt + 1 < kt_end;
+    const bool has2 = kt + 2 < kt_end;
+    if (has2) load_k(kt + 2);
+    if (has1) load_v(kt + 1);
+    if (has1 && live(kt + 1)) scores(kt + 1, nxt);
+    if (live(kt)) softmax_pv(kt, cur);
+    if (has2) store_k(kt & 1);
+    if (has1) store_v((kt + 1) & 1);
+    __syncthreads();
+  };
+
+  if (kt_begin < kt_end) {
+    load_k(kt_begin);
+    load_v(kt_begin);
+    store_k(kt_begin & 1);
+    store_v(kt_begin & 1);
+    if (kt_begin + 1 < kt_end) {
+      load_k(kt_begin + 1);
+      store_k((kt_begin + 1) & 1);
     }
     __syncthreads();
-    if (kt + 1 < kt_end) sstore();
+    if (live(kt_begin)) scores(kt_begin, sa);
+    __syncthreads();  // K(kt_begin)'s buffer is refilled in the first step
+  }
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
+    step(kt, sa, sb);
+    if (kt + 1 < kt_end) step(kt + 1, sb, sa);
   }
 
   // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = pair_sum(lsum);
   if (qi <= last_row) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     uint16_t* optr = p.o + ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D;
@@ -334,14 +392,15 @@ struct FwdF32Params {
   float* lse;
   int l_q, l_k, h, h_kv, grp;
   int n_heads;
-  float c;
+  float c;          // |scale| * log2(e)
+  int neg_scale;    // 1: scale < 0 (Q enters negated)
   int dlo, dhi;
 };
 
 constexpr int kF32Rows = 64;
 constexpr int kF32Keys = 64;
 
-template <int D, bool NEGS>
+template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdF32Params p) {
   constexpr int NC = D / 16;  // float4 chunks per lane
   __shared__ f32x4_t ks[kF32Keys * (D / 4)];
@@ -370,7 +429,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdF32Params p) {
   f32x4_t ov[NC];
 #pragma unroll
   for (int m4 = 0; m4 < NC; ++m4) {
-    qv[m4] = qptr[c + 4 * m4];
+    qv[m4] = p.neg_scale ? -qptr[c + 4 * m4] : qptr[c + 4 * m4];  // fold the sign
     ov[m4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   float m = kNegInf, lsum = 0.f;
@@ -406,7 +465,6 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdF32Params p) {
           }
           acc += __shfl_xor(acc, 1);
           acc += __shfl_xor(acc, 2);
-          if (NEGS) acc = -acc;
           const long long j = j0 + jg + jj;
           const long long rel = j - qi;
           const bool ok = j < p.l_k && rel >= p.dlo && rel <= p.dhi;
@@ -472,18 +530,15 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
   p.xcd_groups = ((s.n * s.h_kv) % 8 == 0) ? 1 : 0;
   p.reverse = s.causal ? 1 : 0;
   p.c = fabsf(s.scale) * kLog2e;
+  p.neg_scale = s.scale < 0.f ? 1 : 0;
   p.dlo = s.dlo;
   p.dhi = s.dhi;
-  const bool negs = s.scale < 0.f;
   dim3 grid((unsigned)p.n_qtiles * (unsigned)p.n_heads);
   dim3 block(kThreads);
-  if (s.d == 128) {
-    if (negs) hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, false>), grid, block, 0, stream, p);
-  } else {
-    if (negs) hipLaunchKernelGGL((fwd_bf16_kernel<64, 128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 128, false>), grid, block, 0, stream, p);
-  }
+  if (s.d == 128)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, 64>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -503,19 +558,16 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
   p.grp = s.h / s.h_kv;
   p.n_heads = s.n * s.h;
   p.c = fabsf(s.scale) * kLog2e;
+  p.neg_scale = s.scale < 0.f ? 1 : 0;
   p.dlo = s.dlo;
   p.dhi = s.dhi;
-  const bool negs = s.scale < 0.f;
   const unsigned tiles = (unsigned)((s.l_q + kF32Rows - 1) / kF32Rows);
   dim3 grid(tiles * (unsigned)p.n_heads);
   dim3 block(256);
-  if (s.d == 128) {
-    if (negs) hipLaunchKernelGGL((fwd_f32_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_f32_kernel<128, false>), grid, block, 0, stream, p);
-  } else {
-    if (negs) hipLaunchKernelGGL((fwd_f32_kernel<64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_f32_kernel<64, false>), grid, block, 0, stream, p);
-  }
+  if (s.d == 128)
+    hipLaunchKernelGGL((fwd_f32_kernel<128>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<64>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
