@@ -43,8 +43,9 @@ struct FwdParams {
   int n_qtiles;
   int xcd_groups;  // 1: keep the workgroups of one key/value head on one XCD
   int reverse;     // 1: launch the last (longest, under causal) q tiles first
-  float c;         // |scale| * log2(e)
-  int neg_scale;   // 1: scale < 0 (Q enters with flipped sign)
+  float c;         // |scale| * log2(e), or log2(e) when scale == 0
+  uint32_t q_and;  // Q fragment mask: 0 when scale == 0
+  uint32_t q_xor;  // Q sign flip: 0x80008000 when scale < 0
   int dlo, dhi;
 };
 
@@ -111,6 +112,12 @@ __device__ __forceinline__ float pair_sum(float x) {
 // fp32 or bf16 range limits.
 constexpr float kRescaleSlack = 8.f;
 
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr bool kUseSched = false;
+
 template <int D, int BN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   static_assert(BN * D / 32 <= kThreads, "at most one V group of 4 keys x 8 dims per thread");
@@ -159,17 +166,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const long long wjlo = max(0LL, (long long)wa + p.dlo);
   const long long wjhi = min((long long)p.l_k - 1, (long long)wb + p.dhi);
 
-  // Q fragment: B operand of S^T = K Q^T, resident for the whole loop.  A
-  // negative scale is folded into Q by flipping its sign bits (exact), so the
-  // scores and c = |scale| log2(e) keep the positive-scale code path.
+  // Q fragment: B operand of S^T = K Q^T, resident for the whole loop.  The
+  // sign of the scale is folded into Q (sign-bit flip, exact) and a zero
+  // scale becomes Q = 0 with c = log2(e) (every allowed score is then 0, as
+  // scale * q.k is), so c > 0 below and a masked score of -inf always gives
+  // exp2(-inf) = 0.
   const size_t q_row = (size_t)p.h * D;
   const uint16_t* qptr = p.q + ((size_t)b * p.l_q + min(qi, last_row)) * q_row +
                          (size_t)hq * D + 8 * half;
-  const uint32_t qsign = p.neg_scale ? 0x80008000u : 0u;
   u32x4_t qf[NDS];
 #pragma unroll
   for (int s = 0; s < NDS; ++s)
-    qf[s] = *reinterpret_cast<const u32x4_t*>(qptr + 16 * s) ^ qsign;
+    qf[s] = (*reinterpret_cast<const u32x4_t*>(qptr + 16 * s) & p.q_and) ^ p.q_xor;
 
   f32x16_t oacc[NDB];
 #pragma unroll
@@ -183,8 +191,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
   const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
 
-  // Register staging (global -> VGPR -> LDS).  K: 16-byte chunks, 16 threads
-  // per row.  V: each thread owns 4 consecutive keys x 8 dims; the 16 (or 32)
+  // Register staging (global -> VGPR -> LDS).  K: 16-byte chunks, D/8
+  // threads per row.  V: each thread owns 4 consecutive keys x 8 dims; the
   // threads of one dim chunk cover consecutive key groups, so the transposed
   // 8-byte LDS writes of a half-wave land on one contiguous V^T row segment.
   u32x4_t kreg[KCH];
@@ -192,6 +200,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int v_kg = tid % (BN / 4);
   const int v_c8 = tid / (BN / 4);
   const int v_pos = vt_pos(4 * v_kg);
+  const bool v_owner = VGROUPS == kThreads || tid < VGROUPS;
+  const uint16_t* vsrc = vbase + v_c8 * 8;
 
   auto load_k = [&](int kt) {
     const int j0 = kt * BN;
@@ -204,14 +214,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       kreg[c] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)j * kv_row + c8 * 8);
     }
   };
-  const bool v_owner = VGROUPS == kThreads || tid < VGROUPS;
   auto load_v = [&](int kt) {
     if (!v_owner) return;
     const int j0 = kt * BN + 4 * v_kg;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = min(j0 + r, p.l_k - 1);
-      vreg[r] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)j * kv_row + v_c8 * 8);
+      vreg[r] = *reinterpret_cast<const u32x4_t*>(vsrc + (size_t)j * kv_row);
     }
   };
   auto store_k = [&](int buf) {
@@ -254,86 +263,94 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       }
     }
   };
-  // Online-softmax update with the tile's scores, then O^T += V^T P^T.
-  auto softmax_pv = [&](int kt, f32x16_t (&sacc)[NKB]) {
+  // Boundary tiles (and tiles outside this wave's band): masked scores -> -inf.
+  auto mask = [&](int kt, f32x16_t (&sacc)[NKB]) {
     const int j0 = kt * BN;
-    const bool full = (j0 + BN <= p.l_k) && ((long long)j0 - wb >= p.dlo) &&
-                      ((long long)(j0 + BN - 1) - wa <= p.dhi);
-    float mx = kNegInf;
-    if (full) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int rel = j - qi;
-          const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
-          sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
-          mx = fmaxf(mx, sacc[kb][r]);
-        }
-    }
-    mx = pair_max(mx);
-    const float mt = (mx == kNegInf) ? kNegInf : mx * p.c;
-    // keep the stale max unless this tile's max exceeds it by the slack
-    const bool grow = mt > m + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      // lanes that keep their max keep alpha = 1 (their m may still be -inf,
-      // and -inf - -inf must not reach the exponential)
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;  // m = -inf -> 0
-      m = grow ? mt : m;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    const float muse = (m == kNegInf) ? 0.f : m;
-    u32x4_t pf[NPS];
-    float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, -muse));
-        float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.c, -muse));
-        if (!full) {
-          p0 = (sacc[kb][r] == kNegInf) ? 0.f : p0;
-          p1 = (sacc[kb][r + 1] == kNegInf) ? 0.f : p1;
-        }
-        rs += p0 + p1;
-        pf[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-      }
-    lsum += rs;
-    const uint16_t* vl = sm.vt[kt & 1];
-#pragma unroll
-    for (int t = 0; t < NPS; ++t)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-            &vl[(32 * db + col) * VS + 16 * t + 8 * half]);
-        oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int rel = j - qi;
+        const bool ok = wave_live && rel >= p.dlo && rel <= p.dhi && j < p.l_k;
+        sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
       }
   };
 
   // Pipeline: while the softmax of tile t runs, the S^T MFMAs of tile t+1 are
-  // already issued; the loads of K(t+2) and V(t+1) are in flight.  K(t+2)
-  // reuses the buffer K(t) had (its scores were taken one step earlier) and
-  // V(t+1) the buffer of V(t-1), so one barrier per tile suffices.
+  // issued in between its VALU work; the loads of K(t+2) and V(t+1) are in
+  // flight.  K(t+2) reuses the buffer K(t) had (its scores were taken one
+  // step earlier) and V(t+1) the buffer of V(t-1), so one barrier per tile
+  // suffices.  Loads and stores past the last tile repeat the last tile
+  // (valid memory, never read), which keeps the step free of branches.
   f32x16_t sa[NKB], sb[NKB];
   auto step = [&](int kt, f32x16_t (&cur)[NKB], f32x16_t (&nxt)[NKB]) {
-    const bool has1 = kt + 1 < kt_end;
-    const bool has2 = kt + 2 < kt_end;
-    if (has2) load_k(kt + 2);
-    if (has1) load_v(kt + 1);
-    if (has1 && live(kt + 1)) scores(kt + 1, nxt);
-    if (live(kt)) softmax_pv(kt, cur);
-    if (has2) store_k(kt & 1);
-    if (has1) store_v((kt + 1) & 1);
+    const int t1 = min(kt + 1, kt_end - 1);
+    const int t2 = min(kt + 2, kt_end - 1);
+    load_k(t2);
+    load_v(t1);
+    if (live(kt) || (kt + 1 < kt_end && live(kt + 1))) {
+      const int j0 = kt * BN;
+      const bool full = live(kt) && (j0 + BN <= p.l_k) &&
+                        ((long long)j0 - wb >= p.dlo) &&
+                        ((long long)(j0 + BN - 1) - wa <= p.dhi);
+      if (!full) mask(kt, cur);
+      // ---- S^T(t+1) MFMAs interleaved with the softmax of tile t
+      scores(kt + 1, nxt);
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+      mx = pair_max(mx);
+      const float mt = mx * p.c;  // c > 0: -inf stays -inf
+      // keep the stale max unless this tile's max exceeds it by the slack;
+      // lanes that keep it have alpha = 1 (their m may still be -inf)
+      const bool grow = mt > m + kRescaleSlack;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+      m = grow ? mt : m;
+      const float muse = (m == kNegInf) ? 0.f : m;
+      u32x4_t pf[NPS];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[kb][r], p.c, -muse));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[kb][r + 1], p.c, -muse));
+          const uint32_t pk = pack_bf16x2(p0, p1);
+          pf[2 * kb + (r >> 3)][(r & 7) >> 1] = pk;
+          // row sum of the bf16 weights the P.V MFMA actually applies
+          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                               __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
+                                               rs, false);
+        }
+      lsum = lsum * alpha + rs;
+#pragma unroll
+      for (int i = 0; i < NKB * NDS; ++i) {
+        if (kUseSched) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        if (kUseSched) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (kUseSched) __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      // ---- O^T += V^T P^T
+      const uint16_t* vl = sm.vt[kt & 1];
+#pragma unroll
+      for (int t = 0; t < NPS; ++t)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+              &vl[(32 * db + col) * VS + 16 * t + 8 * half]);
+          oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
+        }
+    }
+    store_k(kt & 1);
+    store_v((kt + 1) & 1);
     __syncthreads();
   };
 
@@ -342,12 +359,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     load_v(kt_begin);
     store_k(kt_begin & 1);
     store_v(kt_begin & 1);
-    if (kt_begin + 1 < kt_end) {
-      load_k(kt_begin + 1);
-      store_k((kt_begin + 1) & 1);
-    }
+    load_k(min(kt_begin + 1, kt_end - 1));
+    store_k((kt_begin + 1) & 1);
     __syncthreads();
-    if (live(kt_begin)) scores(kt_begin, sa);
+    scores(kt_begin, sa);
     __syncthreads();  // K(kt_begin)'s buffer is refilled in the first step
   }
   for (int kt = kt_begin; kt < kt_end; kt += 2) {
@@ -529,8 +544,9 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
   p.n_qtiles = (s.l_q + kBM - 1) / kBM;
   p.xcd_groups = ((s.n * s.h_kv) % 8 == 0) ? 1 : 0;
   p.reverse = s.causal ? 1 : 0;
-  p.c = fabsf(s.scale) * kLog2e;
-  p.neg_scale = s.scale < 0.f ? 1 : 0;
+  p.c = (s.scale == 0.f ? 1.f : fabsf(s.scale)) * kLog2e;
+  p.q_and = s.scale == 0.f ? 0u : 0xffffffffu;
+  p.q_xor = s.scale < 0.f ? 0x80008000u : 0u;
   p.dlo = s.dlo;
   p.dhi = s.dhi;
   dim3 grid((unsigned)p.n_qtiles * (unsigned)p.n_heads);
