@@ -135,7 +135,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // the wave index is uniform across the wave: keep it (and the band and
+  // tile bookkeeping derived from it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -191,37 +193,45 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
   const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
 
-  // Register staging (global -> VGPR -> LDS).  K: 16-byte chunks, D/8
-  // threads per row.  V: each thread owns 4 consecutive keys x 8 dims; the
-  // threads of one dim chunk cover consecutive key groups, so the transposed
-  // 8-byte LDS writes of a half-wave land on one contiguous V^T row segment.
+  // Register staging (global -> VGPR -> LDS) with buffer loads.  Each tile
+  // gets a buffer descriptor based at its first key row (scalar registers);
+  // a lane's offset inside the tile is fixed, and the hardware range check
+  // returns zeros for rows past l_k, so a tail tile needs no clamping (those
+  // keys are masked anyway).  K: 16-byte chunks, D/8 lanes per row.  V: each
+  // thread owns 4 consecutive keys x 8 dims; the threads of one dim chunk
+  // cover consecutive key groups, so the transposed 8-byte LDS writes of a
+  // half-wave land on one contiguous V^T row segment.
   u32x4_t kreg[KCH];
   u32x4_t vreg[4];
   const int v_kg = tid % (BN / 4);
   const int v_c8 = tid / (BN / 4);
   const int v_pos = vt_pos(4 * v_kg);
   const bool v_owner = VGROUPS == kThreads || tid < VGROUPS;
-  const uint16_t* vsrc = vbase + v_c8 * 8;
+  const uint32_t kv_row_b = (uint32_t)kv_row * 2u;
+  constexpr int KROWS_PER_PASS = kThreads / (D / 8);
+  const uint32_t koff = (uint32_t)(tid / (D / 8)) * kv_row_b + (uint32_t)(tid % (D / 8)) * 16u;
+  const uint32_t voff = (uint32_t)(4 * v_kg) * kv_row_b + (uint32_t)v_c8 * 16u;
 
+  auto tile_rsrc = [&](const uint16_t* base, int kt) {
+    const long long rows = (long long)p.l_k - (long long)kt * BN;
+    const long long bytes = min(rows * (long long)kv_row_b, 0x7fffffffLL);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base + (size_t)kt * BN * kv_row), (short)0, (int)bytes,
+        0x00020000);
+  };
   auto load_k = [&](int kt) {
-    const int j0 = kt * BN;
+    const auto rs = tile_rsrc(kbase, kt);
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int id = tid + c * kThreads;
-      const int row = id / (D / 8);
-      const int c8 = id % (D / 8);
-      const int j = min(j0 + row, p.l_k - 1);
-      kreg[c] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)j * kv_row + c8 * 8);
-    }
+    for (int c = 0; c < KCH; ++c)
+      kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, koff, (uint32_t)(c * KROWS_PER_PASS) * kv_row_b, 0);
   };
   auto load_v = [&](int kt) {
     if (!v_owner) return;
-    const int j0 = kt * BN + 4 * v_kg;
+    const auto rs = tile_rsrc(vbase, kt);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = min(j0 + r, p.l_k - 1);
-      vreg[r] = *reinterpret_cast<const u32x4_t*>(vsrc + (size_t)j * kv_row);
-    }
+    for (int r = 0; r < 4; ++r)
+      vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (uint32_t)r * kv_row_b, 0);
   };
   auto store_k = [&](int buf) {
 #pragma unroll
@@ -235,13 +245,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   auto store_v = [&](int buf) {
     if (!v_owner) return;
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int w = dd >> 1;
-      const int sh = (dd & 1) * 16;
-      u32x2_t pk;
-      pk[0] = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
-      pk[1] = ((vreg[2][w] >> sh) & 0xffffu) | (((vreg[3][w] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<u32x2_t*>(&sm.vt[buf][(v_c8 * 8 + dd) * VS + v_pos]) = pk;
+    for (int w = 0; w < 4; ++w) {
+      // dims 2w (low halves) and 2w+1 (high halves) of the 4 keys
+      u32x2_t lo, hi;
+      lo[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
+      hi[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
+      hi[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
+      *reinterpret_cast<u32x2_t*>(&sm.vt[buf][(v_c8 * 8 + 2 * w) * VS + v_pos]) = lo;
+      *reinterpret_cast<u32x2_t*>(&sm.vt[buf][(v_c8 * 8 + 2 * w + 1) * VS + v_pos]) = hi;
     }
   };
   auto live = [&](int kt) {
