@@ -17,9 +17,10 @@
 //    row sum none until the epilogue.
 //  * O^T = V^T P^T reuses the S^T registers directly as the B operand (the
 //    contraction order over keys is free, so the 8 keys a lane holds become
-//    the 8 k-slots it supplies).  V is stored transposed in LDS with keys
-//    permuted inside each 16-key group so that the matching A operand is one
-//    16-byte LDS read.
+//    the 8 k-slots it supplies).  The matching A operand (8 keys of one dim)
+//    comes from the row-major V tile through two transposing LDS reads.
+//  * K and V tiles of 64 keys are double-buffered in LDS and filled by
+//    direct global-to-LDS buffer loads one tile ahead; one barrier per tile.
 //  * Key tiles wholly outside a workgroup's causal/window band are never
 //    visited; tiles wholly inside run without per-element mask work.
 #include "common.hpp"
@@ -76,21 +77,6 @@ __device__ __forceinline__ void map_block(const FwdParams& p, int& tile,
   tile = p.reverse ? (p.n_qtiles - 1 - rank) : rank;
 }
 
-template <int D, int BN>
-struct __attribute__((aligned(16))) FwdSmem {
-  static constexpr int kKStride = D + 8;   // bf16 per K row (16 B pad)
-  static constexpr int kVStride = BN + 8;  // bf16 per V^T row (16 B pad)
-  uint16_t k[2][BN * kKStride];            // double-buffered K tiles
-  uint16_t vt[2][D * kVStride];            // double-buffered V^T tiles
-};
-
-// Position of key kk (0..BN-1) inside a V^T row: within each group of 16 keys
-// bits 2 and 3 swap, so that keys {4h+0..3, 8+4h+0..3} (what a lane of half h
-// holds after the S^T MFMA) are 8 contiguous elements.
-__device__ __forceinline__ int vt_pos(int kk) {
-  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
-
 // The other half-wave's copy of x (lane l <-> lane l ^ 32), then combined:
 // v_permlane32_swap hands lanes 0-31 the upper half's value in its second
 // result and lanes 32-63 the lower half's value in its first result, so
@@ -112,26 +98,71 @@ __device__ __forceinline__ float pair_sum(float x) {
 // fp32 or bf16 range limits.
 constexpr float kRescaleSlack = 8.f;
 
-// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002;
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-constexpr bool kUseSched = false;
+// Tiles move HBM -> LDS by buffer loads that write LDS directly (no VGPR
+// staging; rows past l_k arrive as zeros).  A tile is stored row-major with
+// unpadded rows whose 16-byte chunks are XOR-swizzled by row, which keeps
+// both readers free of bank conflicts: the S^T MFMA reads K rows as its A
+// operand, and the P.V MFMA reads V transposed with ds_read_b64_tr_b16 (each
+// 16-lane group gathers 4 keys x 4 dims and hands every lane one dim of the
+// 4 keys).
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
+
+// Chunk swizzle of row r.  D = 128 (16 chunks per row): 4 (r % 4) + (r / 4) % 4,
+// so 16 consecutive rows and 4 consecutive rows x 4 chunk pairs each cover
+// all 16 chunk positions.  D = 64 (8 chunks, two rows per 64 banks): the
+// 3-bit reversal of (r / 2) % 8.
+template <int D>
+__device__ __forceinline__ uint32_t chunk_swz(uint32_t r) {
+  if (D == 128) return ((r & 3u) << 2) | ((r >> 2) & 3u);
+  const uint32_t x = (r >> 1) & 7u;
+  return ((x & 1u) << 2) | (x & 2u) | ((x >> 2) & 1u);
+}
+
+
+// Per-lane LDS read addresses of the swizzled tiles.  The swizzle is an XOR
+// on chunk bits, so every address is one base XOR an immediate.
+//  * S^T A operand, slice s: row col (+ 32 kb), logical chunk 2 s + half:
+//      col * RB + 16 ((2 s + half) ^ swz(col)) = ka0 ^ (32 s).
+//  * P.V A operand, transposed read c of slice t for dim block db: the lane
+//    addresses key 16 t + 8 c + 4 h + m and dims 32 db + 16 (G % 2) + 4 a .. +3,
+//    with (G, a, m) = (lane / 16, lane % 4, (lane / 4) % 4) and h = G / 2:
+//      D = 128: key*256 + 16 ((4 db + 2 g2 + a/2) ^ (4 m + (2 c ^ h))) + 8 (a & 1)
+//             = 2048 c + (va0 ^ (64 db + 32 c)),  g2 = G % 2;
+//      D = 64:  key*128 + 16 ((4 db + 2 g2 + a/2) ^ (4 (m/2) + 2 h + c)) + 8 (a & 1)
+//             = 1024 c + (va0 ^ (64 db + 16 c)).
+template <int D>
+__device__ __forceinline__ void lds_read_bases(int lane, uint32_t& ka0, uint32_t& va0) {
+  constexpr uint32_t RB = D * 2;
+  const uint32_t col = (uint32_t)lane & 31u, half = (uint32_t)lane >> 5;
+  ka0 = col * RB | ((half ^ chunk_swz<D>(col)) * 16u);
+  const uint32_t G = (uint32_t)lane >> 4, a = (uint32_t)lane & 3u;
+  const uint32_t mm = ((uint32_t)lane >> 2) & 3u, hh = G >> 1, g2 = G & 1u;
+  const uint32_t z = D == 128 ? ((mm << 2) | ((2u * g2 + (a >> 1)) ^ hh))
+                              : (((mm >> 1) << 2) | ((g2 ^ hh) << 1) | (a >> 1));
+  va0 = (4u * hh + mm) * RB | (z * 16u) | ((a & 1u) * 8u);
+}
 
 template <int D, int BN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
-  static_assert(BN * D / 32 <= kThreads, "at most one V group of 4 keys x 8 dims per thread");
-  static_assert((BN * D / 8) % kThreads == 0, "whole K chunks per thread");
-  constexpr int VGROUPS = BN * D / 32;
-  constexpr int KS = FwdSmem<D, BN>::kKStride;
-  constexpr int VS = FwdSmem<D, BN>::kVStride;
-  constexpr int KCH = BN * D / 8 / kThreads;
+  static_assert(BN == 64, "tile of 64 keys");
+  constexpr int RB = D * 2;          // bytes per tile row
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int ROWS_PER_DMA = 1024 / RB;  // rows one wave-wide DMA writes
+  constexpr int DMA_PER_WAVE = BN / ROWS_PER_DMA / kWaves;
   constexpr int NKB = BN / 32;   // 32-key blocks per tile
   constexpr int NDS = D / 16;    // 16-wide dim slices (S^T MFMA k steps)
   constexpr int NDB = D / 32;    // 32-dim blocks of O^T
   constexpr int NPS = BN / 16;   // 16-key slices (O^T MFMA k steps)
+  constexpr uint32_t kVC = D == 128 ? 32u : 16u;   // chunk-bit flip of read c = 1
 
-  __shared__ FwdSmem<D, BN> sm;
+  // four separate LDS objects, so the compiler can tell the buffer being
+  // read from the one the DMA is filling and need not wait for the DMA
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[BN * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[BN * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[BN * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[BN * D * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -192,128 +223,83 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const size_t kv_row = (size_t)p.h_kv * D;
   const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
   const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
-
-  // Register staging (global -> VGPR -> LDS) with buffer loads.  Each tile
-  // gets a buffer descriptor based at its first key row (scalar registers);
-  // a lane's offset inside the tile is fixed, and the hardware range check
-  // returns zeros for rows past l_k, so a tail tile needs no clamping (those
-  // keys are masked anyway).  K: 16-byte chunks, D/8 lanes per row.  V: each
-  // thread owns 4 consecutive keys x 8 dims; the threads of one dim chunk
-  // cover consecutive key groups, so the transposed 8-byte LDS writes of a
-  // half-wave land on one contiguous V^T row segment.
-  u32x4_t kreg[KCH];
-  u32x4_t vreg[4];
-  const int v_kg = tid % (BN / 4);
-  const int v_c8 = tid / (BN / 4);
-  const int v_pos = vt_pos(4 * v_kg);
-  const bool v_owner = VGROUPS == kThreads || tid < VGROUPS;
   const uint32_t kv_row_b = (uint32_t)kv_row * 2u;
-  constexpr int KROWS_PER_PASS = kThreads / (D / 8);
-  const uint32_t koff = (uint32_t)(tid / (D / 8)) * kv_row_b + (uint32_t)(tid % (D / 8)) * 16u;
-  const uint32_t voff = (uint32_t)(4 * v_kg) * kv_row_b + (uint32_t)v_c8 * 16u;
 
-  auto tile_rsrc = [&](const uint16_t* base, int kt) {
+  // DMA: instruction x of wave w writes rows (kWaves x + w) ROWS_PER_DMA + ...;
+  // each lane fetches the logical chunk the swizzle places at its slot.
+  const uint32_t dma_row = (uint32_t)(wave * ROWS_PER_DMA + lane / CPR);
+  const uint32_t dma_off =
+      dma_row * kv_row_b + (((uint32_t)(lane % CPR)) ^ chunk_swz<D>(dma_row)) * 16u;
+  auto dma_tile = [&](const uint16_t* base, unsigned char* lds, int kt) {
     const long long rows = (long long)p.l_k - (long long)kt * BN;
     const long long bytes = min(rows * (long long)kv_row_b, 0x7fffffffLL);
-    return __builtin_amdgcn_make_buffer_rsrc(
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(base + (size_t)kt * BN * kv_row), (short)0, (int)bytes,
         0x00020000);
-  };
-  auto load_k = [&](int kt) {
-    const auto rs = tile_rsrc(kbase, kt);
 #pragma unroll
-    for (int c = 0; c < KCH; ++c)
-      kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(
-          rs, koff, (uint32_t)(c * KROWS_PER_PASS) * kv_row_b, 0);
-  };
-  auto load_v = [&](int kt) {
-    if (!v_owner) return;
-    const auto rs = tile_rsrc(vbase, kt);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (uint32_t)r * kv_row_b, 0);
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int id = tid + c * kThreads;
-      const int row = id / (D / 8);
-      const int c8 = id % (D / 8);
-      *reinterpret_cast<u32x4_t*>(&sm.k[buf][row * KS + c8 * 8]) = kreg[c];
+    for (int x = 0; x < DMA_PER_WAVE; ++x) {
+      const int row0 = (x * kWaves + wave) * ROWS_PER_DMA;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_ptr)(lds + row0 * RB), 16, dma_off,
+          (uint32_t)(x * kWaves * ROWS_PER_DMA) * kv_row_b, 0, 0);
     }
   };
-  auto store_v = [&](int buf) {
-    if (!v_owner) return;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dims 2w (low halves) and 2w+1 (high halves) of the 4 keys
-      u32x2_t lo, hi;
-      lo[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-      *reinterpret_cast<u32x2_t*>(&sm.vt[buf][(v_c8 * 8 + 2 * w) * VS + v_pos]) = lo;
-      *reinterpret_cast<u32x2_t*>(&sm.vt[buf][(v_c8 * 8 + 2 * w + 1) * VS + v_pos]) = hi;
-    }
+  auto load_tile = [&](int kt, unsigned char* kd, unsigned char* vd) {
+    dma_tile(kbase, kd, kt);
+    dma_tile(vbase, vd, kt);
   };
+
+  uint32_t ka0, va0;
+  lds_read_bases<D>(lane, ka0, va0);
+
   auto live = [&](int kt) {
     const long long j0 = (long long)kt * BN;
     return wave_live && j0 <= wjhi && j0 + BN - 1 >= wjlo;
   };
-  // S^T = K Q^T for one tile: NKB blocks of 32 keys x 32 queries.
-  auto scores = [&](int kt, f32x16_t (&sacc)[NKB]) {
-    const uint16_t* kl = sm.k[kt & 1];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NDS; ++s) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-            &kl[(32 * kb + col) * KS + 16 * s + 8 * half]);
-        sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
-      }
-    }
-  };
-  // Boundary tiles (and tiles outside this wave's band): masked scores -> -inf.
-  auto mask = [&](int kt, f32x16_t (&sacc)[NKB]) {
-    const int j0 = kt * BN;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int rel = j - qi;
-        const bool ok = wave_live && rel >= p.dlo && rel <= p.dhi && j < p.l_k;
-        sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
-      }
-  };
 
-  // Pipeline: while the softmax of tile t runs, the S^T MFMAs of tile t+1 are
-  // issued in between its VALU work; the loads of K(t+2) and V(t+1) are in
-  // flight.  K(t+2) reuses the buffer K(t) had (its scores were taken one
-  // step earlier) and V(t+1) the buffer of V(t-1), so one barrier per tile
-  // suffices.  Loads and stores past the last tile repeat the last tile
-  // (valid memory, never read), which keeps the step free of branches.
-  f32x16_t sa[NKB], sb[NKB];
-  auto step = [&](int kt, f32x16_t (&cur)[NKB], f32x16_t (&nxt)[NKB]) {
-    const int t1 = min(kt + 1, kt_end - 1);
-    const int t2 = min(kt + 2, kt_end - 1);
-    load_k(t2);
-    load_v(t1);
-    if (live(kt) || (kt + 1 < kt_end && live(kt + 1))) {
+  // One tile: S^T = K Q^T, mask (boundary tiles), online softmax, O += P V,
+  // reading buffers (kl, vl).  The DMA of tile kt+1 into the other buffers
+  // (last read for tile kt-1) is in flight meanwhile; the barrier at the end
+  // publishes it.
+  auto step = [&](int kt, const unsigned char* kl, const unsigned char* vl,
+                  unsigned char* kn, unsigned char* vn) {
+    if (kt + 1 < kt_end) load_tile(kt + 1, kn, vn);
+    if (live(kt)) {
+      // the empty asm keeps the derived addresses from being hoisted and
+      // held live across the loop
+      uint32_t ka = ka0, va = va0;
+      asm volatile("" : "+v"(ka), "+v"(va));
+      f32x16_t sacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+              kl + kb * 32 * RB + (ka ^ (32u * s)));
+          sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
+        }
+      }
       const int j0 = kt * BN;
-      const bool full = live(kt) && (j0 + BN <= p.l_k) &&
-                        ((long long)j0 - wb >= p.dlo) &&
+      const bool full = (j0 + BN <= p.l_k) && ((long long)j0 - wb >= p.dlo) &&
                         ((long long)(j0 + BN - 1) - wa <= p.dhi);
-      if (!full) mask(kt, cur);
-      // ---- S^T(t+1) MFMAs interleaved with the softmax of tile t
-      scores(kt + 1, nxt);
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int rel = j - qi;
+            const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
+            sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+          }
+      }
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       mx = pair_max(mx);
       const float mt = mx * p.c;  // c > 0: -inf stays -inf
       // keep the stale max unless this tile's max exceeds it by the slack;
@@ -328,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[kb][r], p.c, -muse));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[kb][r + 1], p.c, -muse));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, -muse));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.c, -muse));
           const uint32_t pk = pack_bf16x2(p0, p1);
           pf[2 * kb + (r >> 3)][(r & 7) >> 1] = pk;
           // row sum of the bf16 weights the P.V MFMA actually applies
@@ -338,48 +324,40 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
                                                rs, false);
         }
       lsum = lsum * alpha + rs;
-#pragma unroll
-      for (int i = 0; i < NKB * NDS; ++i) {
-        if (kUseSched) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        if (kUseSched) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (kUseSched) __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
-      }
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       }
-      // ---- O^T += V^T P^T
-      const uint16_t* vl = sm.vt[kt & 1];
+      // ---- O^T += V^T P^T, V^T read transposed out of the row-major tile
 #pragma unroll
       for (int t = 0; t < NPS; ++t)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              &vl[(32 * db + col) * VS + 16 * t + 8 * half]);
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(vl + t * 16 * RB + (va ^ (64u * db))));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(vl + t * 16 * RB + 8 * RB + (va ^ (64u * db + kVC))));
+          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+          const u32x4_t a = {l2[0], l2[1], h2[0], h2[1]};
           oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
         }
     }
-    store_k(kt & 1);
-    store_v((kt + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA landed
     __syncthreads();
   };
 
   if (kt_begin < kt_end) {
-    load_k(kt_begin);
-    load_v(kt_begin);
-    store_k(kt_begin & 1);
-    store_v(kt_begin & 1);
-    load_k(min(kt_begin + 1, kt_end - 1));
-    store_k((kt_begin + 1) & 1);
+    load_tile(kt_begin, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    scores(kt_begin, sa);
-    __syncthreads();  // K(kt_begin)'s buffer is refilled in the first step
   }
+  // unrolled by two so that every buffer reference is a fixed LDS object
   for (int kt = kt_begin; kt < kt_end; kt += 2) {
-    step(kt, sa, sb);
-    if (kt + 1 < kt_end) step(kt + 1, sb, sa);
+    step(kt, k_lds0, v_lds0, k_lds1, v_lds1);
+    if (kt + 1 < kt_end) step(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
   // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
