@@ -37,7 +37,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 10 times "
+                         "(reference for the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -60,29 +63,62 @@ def timed(fn, steps, warmup, torch):
 
 def cpu_baseline(x, w, seconds):
     """The fp64 oracle, as it stands, on a bounded sample of the workload:
-    whole heads of the same inputs, as many as fit in about `seconds`."""
+    whole (batch, head) pairs of the same inputs, cycling through the batch,
+    until about `seconds` of CPU work is done."""
     import oracle
     from blockwise_exact_attention_amd.flops import allowed_pairs, fwd_flops
+    cores = os.cpu_count() or 1
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] or [1])
+        cores = max([i.get("num_threads", 1) for i in info] or [cores])
     except Exception:
-        cores = os.cpu_count() or 1
+        pass
     pairs = allowed_pairs(w.l_q, w.l_k, True)
     heads_all = [(b, hq) for b in range(w.n) for hq in range(w.h)]
     done = 0
     t0 = time.perf_counter()
-    while done < len(heads_all) and time.perf_counter() - t0 < seconds:
+    while time.perf_counter() - t0 < seconds:
         oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale, True,
-                             heads=[heads_all[done]])
+                             heads=[heads_all[done % len(heads_all)]])
         done += 1
     dt = time.perf_counter() - t0
     flops = fwd_flops(1, done, w.d, pairs)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{done} of {len(heads_all)} (batch, head) pairs of the "
-                      f"same workload, fp64 numpy, {dt:.1f} s"}
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{done} (batch, head) forward passes of this workload "
+                      f"({done / len(heads_all):.2f} x the whole batch), fp64 "
+                      f"numpy, {dt:.1f} s"}
+
+
+def counted_traffic():
+    """HBM bytes per forward launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or
+    None when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "fwd_bf16_causal_mha_n2_l2048_h16_d128_counters.json")
+    src = os.path.join(ROOT, "blockwise_exact_attention_amd", "csrc", "fwd.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("fwd_hip_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of nbytes, ten times: the reference that
+    the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": int(src.numel() * 4), "copies": 10}))
 
 
 def main():
@@ -92,6 +128,9 @@ def main():
               "multi-GPU run of this path is not part of this build",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     from blockwise_exact_attention_amd import attention as A
     from blockwise_exact_attention_amd.flops import (allowed_pairs, fwd_flops,
@@ -115,20 +154,21 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # per-launch durations on the launch stream, over the timed region
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # The timed region: K launches back to back on the launch stream.  One
+    # event pair around them gives the GPU time per launch (the host queues
+    # launches faster than they run); the host clock gives time per step.
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record()
+    start.record()
+    for _ in range(args.steps):
         step()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     ms_step = wall * 1e3 / args.steps
-    kern_ms = float(per.mean())
+    kern_ms = start.elapsed_time(end) / args.steps
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
 
@@ -153,10 +193,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": counted_traffic(),
                      "kernel": "fwd_bf16_kernel<128,64>",
-                     "kernel_ms_mean": round(kern_ms, 5),
-                     "kernel_ms_median": round(float(np.median(per)), 5),
+                     "kernel_ms_per_launch": round(kern_ms, 5),
                      "algorithmic_bytes": fwd_bytes(w.n, w.l_q, w.l_k, w.h,
                                                     w.h_kv, w.d, 2)},
     }
