@@ -144,8 +144,15 @@ __device__ __forceinline__ void lds_read_bases(int lane, uint32_t& ka0, uint32_t
   va0 = (4u * hh + mm) * RB | (z * 16u) | ((a & 1u) * 8u);
 }
 
-template <int D, int BN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
+// KSPLIT = 2: eight waves per workgroup in two groups of four that cover the
+// same 128 query rows and take alternate key tiles, each group with its own
+// LDS buffers and online-softmax state; the two partial rows are merged at
+// the end like two ring chunks.  A q tile then finishes in about half the
+// time with one workgroup per CU, which lets a small or causal-imbalanced
+// grid run longest-first and balance.
+template <int D, int BN, int KSPLIT>
+__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf16_kernel(
+    FwdParams p) {
   static_assert(BN == 64, "tile of 64 keys");
   constexpr int RB = D * 2;          // bytes per tile row
   constexpr int CPR = D / 8;         // 16-byte chunks per row
@@ -157,18 +164,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int NPS = BN / 16;   // 16-key slices (O^T MFMA k steps)
   constexpr uint32_t kVC = D == 128 ? 32u : 16u;   // chunk-bit flip of read c = 1
 
-  // four separate LDS objects, so the compiler can tell the buffer being
-  // read from the one the DMA is filling and need not wait for the DMA
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[BN * D * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[BN * D * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[BN * D * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[BN * D * 2];
+  // four separate LDS objects (one slot per key group in each), so the
+  // compiler can tell the buffer being read from the one the DMA is filling
+  // and need not wait for the DMA
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[KSPLIT][BN * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[KSPLIT][BN * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[KSPLIT][BN * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[KSPLIT][BN * D * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // the wave index is uniform across the wave: keep it (and the band and
   // tile bookkeeping derived from it) in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all / kWaves;   // key group (0 unless KSPLIT = 2)
+  const int wave = wave_all % kWaves;  // query block of this wave
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -258,12 +268,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   };
 
   // One tile: S^T = K Q^T, mask (boundary tiles), online softmax, O += P V,
-  // reading buffers (kl, vl).  The DMA of tile kt+1 into the other buffers
-  // (last read for tile kt-1) is in flight meanwhile; the barrier at the end
-  // publishes it.
+  // reading buffers (kl, vl).  The DMA of this group's next tile into the
+  // other buffers (last read one step earlier) is in flight meanwhile; the
+  // barrier at the end publishes it.
   auto step = [&](int kt, const unsigned char* kl, const unsigned char* vl,
                   unsigned char* kn, unsigned char* vn) {
-    if (kt + 1 < kt_end) load_tile(kt + 1, kn, vn);
+    if (kt + KSPLIT < kt_end) load_tile(kt + KSPLIT, kn, vn);
     if (live(kt)) {
       // the empty asm keeps the derived addresses from being hoisted and
       // held live across the loop
@@ -349,19 +359,65 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
   };
 
+  // this group's tiles: kt_begin + grp + KSPLIT u; every group runs the same
+  // number of steps (and barriers), idling past its last tile
+  const int kt_first = kt_begin + grp;
+  const int n_steps = (kt_end - kt_begin + KSPLIT - 1) / KSPLIT;
   if (kt_begin < kt_end) {
-    load_tile(kt_begin, k_lds0, v_lds0);
+    if (kt_first < kt_end) load_tile(kt_first, k_lds0[grp], v_lds0[grp]);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
   // unrolled by two so that every buffer reference is a fixed LDS object
-  for (int kt = kt_begin; kt < kt_end; kt += 2) {
-    step(kt, k_lds0, v_lds0, k_lds1, v_lds1);
-    if (kt + 1 < kt_end) step(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+  for (int u = 0; u < n_steps; u += 2) {
+    const int kt = kt_first + KSPLIT * u;
+    if (kt < kt_end) step(kt, k_lds0[grp], v_lds0[grp], k_lds1[grp], v_lds1[grp]);
+    else __syncthreads();
+    if (u + 1 < n_steps) {
+      if (kt + KSPLIT < kt_end)
+        step(kt + KSPLIT, k_lds1[grp], v_lds1[grp], k_lds0[grp], v_lds0[grp]);
+      else __syncthreads();
+    }
+  }
+
+  float ltot = pair_sum(lsum);
+  if constexpr (KSPLIT == 2) {
+    // ---- merge group 1's partial rows into group 0's: both shift to the
+    // larger max, through LDS (group 0's first K buffer, 16 floats per lane:
+    // 256 lanes x 64 B = 16 KB, the buffer's size at D = 64): first (m, l),
+    // then one 32-dim block of O at a time
+    static_assert(kThreads * 16 * 4 <= KSPLIT * BN * D * 2, "exchange fits");
+    float* xch = reinterpret_cast<float*>(&k_lds0[0][0]) + (size_t)(wave * 64 + lane) * 16;
+    if (grp == 1) {
+      xch[0] = m;
+      xch[1] = ltot;
+    }
+    __syncthreads();
+    const float m1 = xch[0];
+    const float l1 = xch[1];
+    const float mm = fmaxf(m, m1);
+    const float w0 = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+    const float w1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      if (grp == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[r] = oacc[db][r];
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * w0 + xch[r] * w1;
+      }
+      __syncthreads();
+    }
+    ltot = ltot * w0 + l1 * w1;
+    m = mm;
+    if (grp == 1) return;
   }
 
   // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
-  const float ltot = pair_sum(lsum);
   if (qi <= last_row) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     uint16_t* optr = p.o + ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D;
@@ -540,11 +596,20 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
   p.dlo = s.dlo;
   p.dhi = s.dhi;
   dim3 grid((unsigned)p.n_qtiles * (unsigned)p.n_heads);
-  dim3 block(kThreads);
-  if (s.d == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, 64>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), grid, block, 0, stream, p);
+  // With no more workgroups than CUs (256), two per CU cannot fill the chip:
+  // split each q tile's keys over two groups of a workgroup instead.
+  const bool split = (long long)p.n_qtiles * p.n_heads <= 256;
+  if (split) {
+    if (s.d == 128)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 2>), grid, dim3(2 * kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 2>), grid, dim3(2 * kThreads), 0, stream, p);
+  } else {
+    if (s.d == 128)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 1>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 1>), grid, dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
