@@ -18,33 +18,88 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 constexpr int kMergeMaxRows = 256;
+constexpr int kMergeElems = 8192;  // elements per block on the vector path
+constexpr int kMergeVec = kMergeElems / (4 * kMergeThreads);  // float4 per thread
 
-// Row modes: 0 keep the accumulator, 1 take the block, 2 weighted sum.
+// Row weights: mode 0 keep the accumulator, 1 take the block, 2 weighted
+// sum.  Computed once per row by one thread and shared through LDS; that
+// thread also writes the row's new LSE (no other thread reads it).
+__device__ __forceinline__ void merge_row_weights(float* __restrict__ lse_acc,
+                                                  const float* __restrict__ lse_blk,
+                                                  int l, int h, long long row,
+                                                  int& mode, float& wa, float& wb) {
+  // rows are ordered (b, i, hq) like O; the LSE of that row sits at [b, hq, i]
+  const long long bi = row / h;
+  const int hq = (int)(row - bi * h);
+  const long long b = bi / l;
+  const int i = (int)(bi - b * l);
+  const size_t li = ((size_t)b * h + hq) * l + i;
+  const float a = lse_acc[li];
+  const float bb = lse_blk[li];
+  wa = 0.f;
+  wb = 0.f;
+  if (bb == kNegInf) {
+    mode = 0;
+  } else if (a == kNegInf) {
+    mode = 1;
+    lse_acc[li] = bb;
+  } else {
+    mode = 2;
+    const float mx = fmaxf(a, bb);
+    const float mn = fminf(a, bb);
+    const float lse = mx + log1pf(expf(mn - mx));
+    wa = expf(a - lse);
+    wb = expf(bb - lse);
+    lse_acc[li] = lse;
+  }
+}
+
+// Vector path (d % 4 == 0, 8192 / d rows per block): a block covers
+// consecutive query rows i0 .. i0 + R - 1 of one (batch, head), so its LSE
+// reads are contiguous; its O rows are R rows h*d apart, each row contiguous.
+// Every thread issues its data loads (the block's values and, speculatively,
+// the accumulator's) before the row weights are known, so a block pays one
+// memory round trip, not two.
 template <bool BLK_BF16>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
     float* __restrict__ acc, float* __restrict__ lse_acc,
     const void* __restrict__ blk, const float* __restrict__ lse_blk, int l,
-    int h, int d, long long rows_total, int rows_per_block) {
+    int h, int d, int iblocks) {
   __shared__ float s_wa[kMergeMaxRows];
   __shared__ float s_wb[kMergeMaxRows];
   __shared__ int s_mode[kMergeMaxRows];
-
-  const long long r0 = (long long)blockIdx.x * rows_per_block;
-  const int nr = (int)min((long long)rows_per_block, rows_total - r0);
+  const int R = kMergeElems / d;
+  const int bh = blockIdx.x / iblocks;       // b * h + hq
+  const int i0 = (blockIdx.x - bh * iblocks) * R;
+  const int b = bh / h;
+  const int hq = bh - b * h;
+  const int nr = min(R, l - i0);
   const int tid = threadIdx.x;
+  const size_t row_stride = (size_t)h * d;
+  const size_t base = ((size_t)b * l + i0) * row_stride + (size_t)hq * d;
 
+  f32x4_t av[kMergeVec], bv[kMergeVec];
+#pragma unroll
+  for (int v = 0; v < kMergeVec; ++v) {
+    const int e = (v * kMergeThreads + tid) * 4;
+    const int rr = e / d;
+    if (rr < nr) {
+      const size_t off = base + (size_t)rr * row_stride + (e - rr * d);
+      if (BLK_BF16) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(
+            static_cast<const uint16_t*>(blk) + off);
+        bv[v] = f32x4_t{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+      } else {
+        bv[v] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(blk) + off);
+      }
+      av[v] = *reinterpret_cast<const f32x4_t*>(acc + off);
+    }
+  }
   if (tid < nr) {
-    // rows are ordered (b, i, hq) like O; the LSE of that row sits at
-    // [b, hq, i]
-    const long long row = r0 + tid;
-    const long long bi = row / h;
-    const int hq = (int)(row - bi * h);
-    const long long b = bi / l;
-    const int i = (int)(bi - b * l);
-    const size_t li = ((size_t)b * h + hq) * l + i;
+    const size_t li = (size_t)bh * l + i0 + tid;
     const float a = lse_acc[li];
     const float bb = lse_blk[li];
-    int mode;
+    int mode = 2;
     float wa = 0.f, wb = 0.f;
     if (bb == kNegInf) {
       mode = 0;
@@ -52,7 +107,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
       mode = 1;
       lse_acc[li] = bb;
     } else {
-      mode = 2;
       const float mx = fmaxf(a, bb);
       const float mn = fminf(a, bb);
       const float lse = mx + log1pf(expf(mn - mx));
@@ -65,40 +119,55 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     s_wb[tid] = wb;
   }
   __syncthreads();
+#pragma unroll
+  for (int v = 0; v < kMergeVec; ++v) {
+    const int e = (v * kMergeThreads + tid) * 4;
+    const int rr = e / d;
+    if (rr >= nr) continue;
+    const int mode = s_mode[rr];
+    const size_t off = base + (size_t)rr * row_stride + (e - rr * d);
+    // a row whose accumulator LSE is -inf takes the block as is (select,
+    // never a multiply, so whatever the accumulator held cannot leak)
+    if (mode == 1)
+      *reinterpret_cast<f32x4_t*>(acc + off) = bv[v];
+    else if (mode == 2)
+      *reinterpret_cast<f32x4_t*>(acc + off) = av[v] * s_wa[rr] + bv[v] * s_wb[rr];
+  }
+}
+
+// Scalar path for any other d: a block covers up to 1024 / d rows.
+template <bool BLK_BF16>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    float* __restrict__ acc, float* __restrict__ lse_acc,
+    const void* __restrict__ blk, const float* __restrict__ lse_blk, int l,
+    int h, int d, long long rows_total, int rows_per_block) {
+  __shared__ float s_wa[kMergeMaxRows];
+  __shared__ float s_wb[kMergeMaxRows];
+  __shared__ int s_mode[kMergeMaxRows];
+
+  const long long r0 = (long long)blockIdx.x * rows_per_block;
+  const int nr = (int)min((long long)rows_per_block, rows_total - r0);
+  const int tid = threadIdx.x;
+  if (tid < nr) {
+    int mode;
+    float wa, wb;
+    merge_row_weights(lse_acc, lse_blk, l, h, r0 + tid, mode, wa, wb);
+    s_mode[tid] = mode;
+    s_wa[tid] = wa;
+    s_wb[tid] = wb;
+  }
+  __syncthreads();
 
   const size_t e0 = (size_t)r0 * d;
   const int ne = nr * d;
-  if ((d & 3) == 0) {
-    for (int e = tid * 4; e < ne; e += kMergeThreads * 4) {
-      const int rr = e / d;
-      const int mode = s_mode[rr];
-      if (mode == 0) continue;
-      f32x4_t bv;
-      if (BLK_BF16) {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(
-            static_cast<const uint16_t*>(blk) + e0 + e);
-        bv = f32x4_t{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-      } else {
-        bv = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(blk) + e0 + e);
-      }
-      f32x4_t* ap = reinterpret_cast<f32x4_t*>(acc + e0 + e);
-      if (mode == 1) {
-        *ap = bv;
-      } else {
-        const f32x4_t av = *ap;
-        *ap = av * s_wa[rr] + bv * s_wb[rr];
-      }
-    }
-  } else {
-    for (int e = tid; e < ne; e += kMergeThreads) {
-      const int rr = e / d;
-      const int mode = s_mode[rr];
-      if (mode == 0) continue;
-      const float bv = BLK_BF16
-          ? bf16_lo(static_cast<const uint16_t*>(blk)[e0 + e])
-          : static_cast<const float*>(blk)[e0 + e];
-      acc[e0 + e] = (mode == 1) ? bv : acc[e0 + e] * s_wa[rr] + bv * s_wb[rr];
-    }
+  for (int e = tid; e < ne; e += kMergeThreads) {
+    const int rr = e / d;
+    const int mode = s_mode[rr];
+    if (mode == 0) continue;
+    const float bv = BLK_BF16
+        ? bf16_lo(static_cast<const uint16_t*>(blk)[e0 + e])
+        : static_cast<const float*>(blk)[e0 + e];
+    acc[e0 + e] = (mode == 1) ? bv : acc[e0 + e] * s_wa[rr] + bv * s_wb[rr];
   }
 }
 
@@ -157,6 +226,19 @@ hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
                         const float* lse_blk, int n, int l, int h, int d,
                         bool blk_bf16, hipStream_t stream) {
   const long long rows = (long long)n * l * h;
+  if (d % 4 == 0 && d <= kMergeElems && kMergeElems % d == 0 &&
+      kMergeElems / d <= kMergeMaxRows) {
+    const int rpb = kMergeElems / d;
+    const int iblocks = (l + rpb - 1) / rpb;
+    dim3 grid((unsigned)((long long)n * h * iblocks)), block(kMergeThreads);
+    if (blk_bf16)
+      hipLaunchKernelGGL((merge_vec_kernel<true>), grid, block, 0, stream, out_acc,
+                         lse_acc, out_blk, lse_blk, l, h, d, iblocks);
+    else
+      hipLaunchKernelGGL((merge_vec_kernel<false>), grid, block, 0, stream, out_acc,
+                         lse_acc, out_blk, lse_blk, l, h, d, iblocks);
+    return hipGetLastError();
+  }
   int rpb = 1024 / d;
   if (rpb < 1) rpb = 1;
   if (rpb > kMergeMaxRows) rpb = kMergeMaxRows;
