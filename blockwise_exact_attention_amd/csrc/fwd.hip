@@ -23,6 +23,8 @@
 //    direct global-to-LDS buffer loads one tile ahead; one barrier per tile.
 //  * Key tiles wholly outside a workgroup's causal/window band are never
 //    visited; tiles wholly inside run without per-element mask work.
+//  * The normalised O rows leave through LDS, so that each global store
+//    writes whole rows rather than 16-byte pieces of 32 rows.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -42,6 +44,8 @@ struct FwdParams {
   int l_q, l_k, h, h_kv, grp;
   int n_heads;     // n * h
   int n_qtiles;
+  int n_units;     // workgroups per head: n_qtiles, or ceil(n_qtiles / 2) paired
+  int pairs;       // 1: workgroup r takes q tiles n_qtiles-1-r and r
   int xcd_groups;  // 1: keep the workgroups of one key/value head on one XCD
   int reverse;     // 1: launch the last (longest, under causal) q tiles first
   float c;         // |scale| * log2(e), or log2(e) when scale == 0
@@ -50,14 +54,16 @@ struct FwdParams {
   int dlo, dhi;
 };
 
-// blockIdx.x -> (q tile, flattened head b*h + hq).
+// blockIdx.x -> (work unit, flattened head b*h + hq); a unit is one q tile,
+// or under pairing the two q tiles n_qtiles-1-r and r, whose key counts add up
+// to about the same total for every r under a causal mask.
 //
 // Workgroups are handed to the 8 XCDs round-robin by id, and each XCD has its
 // own L2.  When the key/value groups split evenly over the XCDs, every
 // workgroup that reads one key/value head is given an id of the same residue
 // mod 8, so that head's K/V tiles are fetched into one L2 only.  Under causal
 // masking the last q tiles see the most keys; they get the lowest ids.
-__device__ __forceinline__ void map_block(const FwdParams& p, int& tile,
+__device__ __forceinline__ void map_block(const FwdParams& p, int& unit,
                                           int& head) {
   const int w = blockIdx.x;
   int rank;
@@ -74,7 +80,7 @@ __device__ __forceinline__ void map_block(const FwdParams& p, int& tile,
     rank = w / p.n_heads;
     head = w - rank * p.n_heads;
   }
-  tile = p.reverse ? (p.n_qtiles - 1 - rank) : rank;
+  unit = p.reverse ? (p.n_units - 1 - rank) : rank;
 }
 
 // The other half-wave's copy of x (lane l <-> lane l ^ 32), then combined:
@@ -149,7 +155,8 @@ __device__ __forceinline__ void lds_read_bases(int lane, uint32_t& ka0, uint32_t
 // LDS buffers and online-softmax state; the two partial rows are merged at
 // the end like two ring chunks.  A q tile then finishes in about half the
 // time with one workgroup per CU, which lets a small or causal-imbalanced
-// grid run longest-first and balance.
+// grid run longest-first and balance.  Under pairing a workgroup takes two q
+// tiles one after the other (the long and the short one of a causal pair).
 template <int D, int BN, int KSPLIT>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf16_kernel(
     FwdParams p) {
@@ -182,260 +189,293 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  int tile, head;
-  map_block(p, tile, head);
-  const int b = head / p.h;
-  const int hq = head - b * p.h;
-  const int g = hq / p.grp;
+  // one q tile: the whole key loop, the merge of the key groups and the
+  // epilogue
+  auto fwd_tile = [&](const int tile, const int head) {
+    const int b = head / p.h;
+    const int hq = head - b * p.h;
+    const int g = hq / p.grp;
 
-  const int last_row = p.l_q - 1;
-  const int i0 = tile * kBM;
-  const int iw = i0 + wave * 32;
-  const int qi = iw + col;
+    const int last_row = p.l_q - 1;
+    const int i0 = tile * kBM;
+    const int iw = i0 + wave * 32;
+    const int qi = iw + col;
 
-  // Key-tile range of the workgroup (rows i0 .. min(i0+kBM, l_q)-1).
-  const long long jlo = max(0LL, (long long)i0 + p.dlo);
-  const long long jhi = min((long long)p.l_k - 1,
-                            (long long)min(i0 + kBM - 1, last_row) + p.dhi);
-  int kt_begin = 0, kt_end = 0;
-  if (jlo <= jhi) {
-    kt_begin = (int)(jlo / BN);
-    kt_end = (int)(jhi / BN) + 1;
-  }
-  // Key range of this wave.
-  const int wa = iw;
-  const int wb = min(iw + 31, last_row);
-  const bool wave_live = wa <= last_row;
-  const long long wjlo = max(0LL, (long long)wa + p.dlo);
-  const long long wjhi = min((long long)p.l_k - 1, (long long)wb + p.dhi);
-
-  // Q fragment: B operand of S^T = K Q^T, resident for the whole loop.  The
-  // sign of the scale is folded into Q (sign-bit flip, exact) and a zero
-  // scale becomes Q = 0 with c = log2(e) (every allowed score is then 0, as
-  // scale * q.k is), so c > 0 below and a masked score of -inf always gives
-  // exp2(-inf) = 0.
-  const size_t q_row = (size_t)p.h * D;
-  const uint16_t* qptr = p.q + ((size_t)b * p.l_q + min(qi, last_row)) * q_row +
-                         (size_t)hq * D + 8 * half;
-  u32x4_t qf[NDS];
-#pragma unroll
-  for (int s = 0; s < NDS; ++s)
-    qf[s] = (*reinterpret_cast<const u32x4_t*>(qptr + 16 * s) & p.q_and) ^ p.q_xor;
-
-  f32x16_t oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m = kNegInf;  // row max used for the exponentials (log2 units)
-  float lsum = 0.f;   // this lane's half of the running row sum
-
-  const size_t kv_row = (size_t)p.h_kv * D;
-  const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
-  const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
-  const uint32_t kv_row_b = (uint32_t)kv_row * 2u;
-
-  // DMA: instruction x of wave w writes rows (kWaves x + w) ROWS_PER_DMA + ...;
-  // each lane fetches the logical chunk the swizzle places at its slot.
-  const uint32_t dma_row = (uint32_t)(wave * ROWS_PER_DMA + lane / CPR);
-  const uint32_t dma_off =
-      dma_row * kv_row_b + (((uint32_t)(lane % CPR)) ^ chunk_swz<D>(dma_row)) * 16u;
-  auto dma_tile = [&](const uint16_t* base, unsigned char* lds, int kt) {
-    const long long rows = (long long)p.l_k - (long long)kt * BN;
-    const long long bytes = min(rows * (long long)kv_row_b, 0x7fffffffLL);
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(base + (size_t)kt * BN * kv_row), (short)0, (int)bytes,
-        0x00020000);
-#pragma unroll
-    for (int x = 0; x < DMA_PER_WAVE; ++x) {
-      const int row0 = (x * kWaves + wave) * ROWS_PER_DMA;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void_ptr)(lds + row0 * RB), 16, dma_off,
-          (uint32_t)(x * kWaves * ROWS_PER_DMA) * kv_row_b, 0, 0);
+    // Key-tile range of the workgroup (rows i0 .. min(i0+kBM, l_q)-1).
+    const long long jlo = max(0LL, (long long)i0 + p.dlo);
+    const long long jhi = min((long long)p.l_k - 1,
+                              (long long)min(i0 + kBM - 1, last_row) + p.dhi);
+    int kt_begin = 0, kt_end = 0;
+    if (jlo <= jhi) {
+      kt_begin = (int)(jlo / BN);
+      kt_end = (int)(jhi / BN) + 1;
     }
-  };
-  auto load_tile = [&](int kt, unsigned char* kd, unsigned char* vd) {
-    dma_tile(kbase, kd, kt);
-    dma_tile(vbase, vd, kt);
-  };
+    // Key range of this wave.
+    const int wa = iw;
+    const int wb = min(iw + 31, last_row);
+    const bool wave_live = wa <= last_row;
+    const long long wjlo = max(0LL, (long long)wa + p.dlo);
+    const long long wjhi = min((long long)p.l_k - 1, (long long)wb + p.dhi);
 
-  uint32_t ka0, va0;
-  lds_read_bases<D>(lane, ka0, va0);
+    // Q fragment: B operand of S^T = K Q^T, resident for the whole loop.  The
+    // sign of the scale is folded into Q (sign-bit flip, exact) and a zero
+    // scale becomes Q = 0 with c = log2(e) (every allowed score is then 0, as
+    // scale * q.k is), so c > 0 below and a masked score of -inf always gives
+    // exp2(-inf) = 0.
+    const size_t q_row = (size_t)p.h * D;
+    const uint16_t* qptr = p.q + ((size_t)b * p.l_q + min(qi, last_row)) * q_row +
+                           (size_t)hq * D + 8 * half;
+    u32x4_t qf[NDS];
+  #pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      qf[s] = (*reinterpret_cast<const u32x4_t*>(qptr + 16 * s) & p.q_and) ^ p.q_xor;
 
-  auto live = [&](int kt) {
-    const long long j0 = (long long)kt * BN;
-    return wave_live && j0 <= wjhi && j0 + BN - 1 >= wjlo;
-  };
+    f32x16_t oacc[NDB];
+  #pragma unroll
+    for (int db = 0; db < NDB; ++db)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m = kNegInf;  // row max used for the exponentials (log2 units)
+    float lsum = 0.f;   // this lane's half of the running row sum
 
-  // One tile: S^T = K Q^T, mask (boundary tiles), online softmax, O += P V,
-  // reading buffers (kl, vl).  The DMA of this group's next tile into the
-  // other buffers (last read one step earlier) is in flight meanwhile; the
-  // barrier at the end publishes it.
-  auto step = [&](int kt, const unsigned char* kl, const unsigned char* vl,
-                  unsigned char* kn, unsigned char* vn) {
-    if (kt + KSPLIT < kt_end) load_tile(kt + KSPLIT, kn, vn);
-    if (live(kt)) {
-      // the empty asm keeps the derived addresses from being hoisted and
-      // held live across the loop
-      uint32_t ka = ka0, va = va0;
-      asm volatile("" : "+v"(ka), "+v"(va));
-      f32x16_t sacc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < NDS; ++s) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              kl + kb * 32 * RB + (ka ^ (32u * s)));
-          sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
-        }
+    const size_t kv_row = (size_t)p.h_kv * D;
+    const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
+    const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
+    const uint32_t kv_row_b = (uint32_t)kv_row * 2u;
+
+    // DMA: instruction x of wave w writes rows (kWaves x + w) ROWS_PER_DMA + ...;
+    // each lane fetches the logical chunk the swizzle places at its slot.
+    const uint32_t dma_row = (uint32_t)(wave * ROWS_PER_DMA + lane / CPR);
+    const uint32_t dma_off =
+        dma_row * kv_row_b + (((uint32_t)(lane % CPR)) ^ chunk_swz<D>(dma_row)) * 16u;
+    auto dma_tile = [&](const uint16_t* base, unsigned char* lds, int kt) {
+      const long long rows = (long long)p.l_k - (long long)kt * BN;
+      const long long bytes = min(rows * (long long)kv_row_b, 0x7fffffffLL);
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(base + (size_t)kt * BN * kv_row), (short)0, (int)bytes,
+          0x00020000);
+  #pragma unroll
+      for (int x = 0; x < DMA_PER_WAVE; ++x) {
+        const int row0 = (x * kWaves + wave) * ROWS_PER_DMA;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void_ptr)(lds + row0 * RB), 16, dma_off,
+            (uint32_t)(x * kWaves * ROWS_PER_DMA) * kv_row_b, 0, 0);
       }
-      const int j0 = kt * BN;
-      const bool full = (j0 + BN <= p.l_k) && ((long long)j0 - wb >= p.dlo) &&
-                        ((long long)(j0 + BN - 1) - wa <= p.dhi);
-      if (!full) {
-#pragma unroll
+    };
+    auto load_tile = [&](int kt, unsigned char* kd, unsigned char* vd) {
+      dma_tile(kbase, kd, kt);
+      dma_tile(vbase, vd, kt);
+    };
+
+    uint32_t ka0, va0;
+    lds_read_bases<D>(lane, ka0, va0);
+
+    auto live = [&](int kt) {
+      const long long j0 = (long long)kt * BN;
+      return wave_live && j0 <= wjhi && j0 + BN - 1 >= wjlo;
+    };
+
+    // One tile: S^T = K Q^T, mask (boundary tiles), online softmax, O += P V,
+    // reading buffers (kl, vl).  The DMA of this group's next tile into the
+    // other buffers (last read one step earlier) is in flight meanwhile; the
+    // barrier at the end publishes it.
+    auto step = [&](int kt, const unsigned char* kl, const unsigned char* vl,
+                    unsigned char* kn, unsigned char* vn) {
+      if (kt + KSPLIT < kt_end) load_tile(kt + KSPLIT, kn, vn);
+      if (live(kt)) {
+        // the empty asm keeps the derived addresses from being hoisted and
+        // held live across the loop
+        uint32_t ka = ka0, va = va0;
+        asm volatile("" : "+v"(ka), "+v"(va));
+        f32x16_t sacc[NKB];
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+  #pragma unroll
+          for (int s = 0; s < NDS; ++s) {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+                kl + kb * 32 * RB + (ka ^ (32u * s)));
+            sacc[kb] = mfma32x32x16(a, qf[s], sacc[kb]);
+          }
+        }
+        const int j0 = kt * BN;
+        const bool full = (j0 + BN <= p.l_k) && ((long long)j0 - wb >= p.dlo) &&
+                          ((long long)(j0 + BN - 1) - wa <= p.dhi);
+        if (!full) {
+  #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+              const int rel = j - qi;
+              const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
+              sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+            }
+        }
+        float mx = kNegInf;
+  #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const int rel = j - qi;
-            const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
-            sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = pair_max(mx);
+        const float mt = mx * p.c;  // c > 0: -inf stays -inf
+        // keep the stale max unless this tile's max exceeds it by the slack;
+        // lanes that keep it have alpha = 1 (their m may still be -inf)
+        const bool grow = mt > m + kRescaleSlack;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+        m = grow ? mt : m;
+        const float muse = (m == kNegInf) ? 0.f : m;
+        u32x4_t pf[NPS];
+        float rs = 0.f;
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, -muse));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.c, -muse));
+            const uint32_t pk = pack_bf16x2(p0, p1);
+            pf[2 * kb + (r >> 3)][(r & 7) >> 1] = pk;
+            // row sum of the bf16 weights the P.V MFMA actually applies
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                                 __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
+                                                 rs, false);
+          }
+        lsum = lsum * alpha + rs;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+  #pragma unroll
+          for (int db = 0; db < NDB; ++db)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        // ---- O^T += V^T P^T, V^T read transposed out of the row-major tile
+  #pragma unroll
+        for (int t = 0; t < NPS; ++t)
+  #pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(vl + t * 16 * RB + (va ^ (64u * db))));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(vl + t * 16 * RB + 8 * RB + (va ^ (64u * db + kVC))));
+            const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+            const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+            const u32x4_t a = {l2[0], l2[1], h2[0], h2[1]};
+            oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
           }
       }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = pair_max(mx);
-      const float mt = mx * p.c;  // c > 0: -inf stays -inf
-      // keep the stale max unless this tile's max exceeds it by the slack;
-      // lanes that keep it have alpha = 1 (their m may still be -inf)
-      const bool grow = mt > m + kRescaleSlack;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
-      m = grow ? mt : m;
-      const float muse = (m == kNegInf) ? 0.f : m;
-      u32x4_t pf[NPS];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, -muse));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.c, -muse));
-          const uint32_t pk = pack_bf16x2(p0, p1);
-          pf[2 * kb + (r >> 3)][(r & 7) >> 1] = pk;
-          // row sum of the bf16 weights the P.V MFMA actually applies
-          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
-                                               __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
-                                               rs, false);
-        }
-      lsum = lsum * alpha + rs;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      // ---- O^T += V^T P^T, V^T read transposed out of the row-major tile
-#pragma unroll
-      for (int t = 0; t < NPS; ++t)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_ptr)(vl + t * 16 * RB + (va ^ (64u * db))));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_ptr)(vl + t * 16 * RB + 8 * RB + (va ^ (64u * db + kVC))));
-          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
-          const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
-          const u32x4_t a = {l2[0], l2[1], h2[0], h2[1]};
-          oacc[db] = mfma32x32x16(a, pf[t], oacc[db]);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA landed
-    __syncthreads();
-  };
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's DMA landed
+      __syncthreads();
+    };
 
-  // this group's tiles: kt_begin + grp + KSPLIT u; every group runs the same
-  // number of steps (and barriers), idling past its last tile
-  const int kt_first = kt_begin + grp;
-  const int n_steps = (kt_end - kt_begin + KSPLIT - 1) / KSPLIT;
-  if (kt_begin < kt_end) {
-    if (kt_first < kt_end) load_tile(kt_first, k_lds0[grp], v_lds0[grp]);
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-  }
-  // unrolled by two so that every buffer reference is a fixed LDS object
-  for (int u = 0; u < n_steps; u += 2) {
-    const int kt = kt_first + KSPLIT * u;
-    if (kt < kt_end) step(kt, k_lds0[grp], v_lds0[grp], k_lds1[grp], v_lds1[grp]);
-    else __syncthreads();
-    if (u + 1 < n_steps) {
-      if (kt + KSPLIT < kt_end)
-        step(kt + KSPLIT, k_lds1[grp], v_lds1[grp], k_lds0[grp], v_lds0[grp]);
+    // this group's tiles: kt_begin + grp + KSPLIT u; every group runs the same
+    // number of steps (and barriers), idling past its last tile
+    const int kt_first = kt_begin + grp;
+    const int n_steps = (kt_end - kt_begin + KSPLIT - 1) / KSPLIT;
+    if (kt_begin < kt_end) {
+      if (kt_first < kt_end) load_tile(kt_first, k_lds0[grp], v_lds0[grp]);
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+    }
+    // unrolled by two so that every buffer reference is a fixed LDS object
+    for (int u = 0; u < n_steps; u += 2) {
+      const int kt = kt_first + KSPLIT * u;
+      if (kt < kt_end) step(kt, k_lds0[grp], v_lds0[grp], k_lds1[grp], v_lds1[grp]);
       else __syncthreads();
+      if (u + 1 < n_steps) {
+        if (kt + KSPLIT < kt_end)
+          step(kt + KSPLIT, k_lds1[grp], v_lds1[grp], k_lds0[grp], v_lds0[grp]);
+        else __syncthreads();
+      }
     }
-  }
 
-  float ltot = pair_sum(lsum);
-  if constexpr (KSPLIT == 2) {
-    // ---- merge group 1's partial rows into group 0's: both shift to the
-    // larger max, through LDS (group 0's first K buffer, 16 floats per lane:
-    // 256 lanes x 64 B = 16 KB, the buffer's size at D = 64): first (m, l),
-    // then one 32-dim block of O at a time
-    static_assert(kThreads * 16 * 4 <= KSPLIT * BN * D * 2, "exchange fits");
-    float* xch = reinterpret_cast<float*>(&k_lds0[0][0]) + (size_t)(wave * 64 + lane) * 16;
-    if (grp == 1) {
-      xch[0] = m;
-      xch[1] = ltot;
-    }
-    __syncthreads();
-    const float m1 = xch[0];
-    const float l1 = xch[1];
-    const float mm = fmaxf(m, m1);
-    const float w0 = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
-    const float w1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-    __syncthreads();
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    float ltot = pair_sum(lsum);
+    if constexpr (KSPLIT == 2) {
+      // ---- merge group 1's partial rows into group 0's (both shift to the
+      // larger max) through LDS in one round: group 1 stores its O
+      // accumulators (float4 f = 4 db + r4 of lane wl at (f, wl), spread over
+      // the two V buffers) and (m, l) (group 1's slot of the second K buffer)
+      const int wl = wave * 64 + lane;
+      float4* xo0 = reinterpret_cast<float4*>(&v_lds0[0][0]);
+      float4* xo1 = reinterpret_cast<float4*>(&v_lds1[0][0]);
+      float2* xml = reinterpret_cast<float2*>(&k_lds1[1][0]) + wl;
+      static_assert(NDB * 2 * kThreads * 16 <= KSPLIT * BN * D * 2, "exchange fits");
       if (grp == 1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xch[r] = oacc[db][r];
+        for (int f = 0; f < 4 * NDB; ++f) {
+          const float4 x = {oacc[f / 4][4 * (f % 4)], oacc[f / 4][4 * (f % 4) + 1],
+                            oacc[f / 4][4 * (f % 4) + 2], oacc[f / 4][4 * (f % 4) + 3]};
+          (f < 2 * NDB ? xo0 : xo1)[(f % (2 * NDB)) * kThreads + wl] = x;
+        }
+        *xml = make_float2(m, ltot);
       }
       __syncthreads();
-      if (grp == 0) {
+      if (grp == 1) return;
+      const float2 ml1 = *xml;
+      const float mm = fmaxf(m, ml1.x);
+      const float w0 = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+      const float w1 = (ml1.x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml1.x - mm);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * w0 + xch[r] * w1;
+      for (int f = 0; f < 4 * NDB; ++f) {
+        const float4 x = (f < 2 * NDB ? xo0 : xo1)[(f % (2 * NDB)) * kThreads + wl];
+        oacc[f / 4][4 * (f % 4)] = oacc[f / 4][4 * (f % 4)] * w0 + x.x * w1;
+        oacc[f / 4][4 * (f % 4) + 1] = oacc[f / 4][4 * (f % 4) + 1] * w0 + x.y * w1;
+        oacc[f / 4][4 * (f % 4) + 2] = oacc[f / 4][4 * (f % 4) + 2] * w0 + x.z * w1;
+        oacc[f / 4][4 * (f % 4) + 3] = oacc[f / 4][4 * (f % 4) + 3] * w0 + x.w * w1;
       }
-      __syncthreads();
+      ltot = ltot * w0 + ml1.y * w1;
+      m = mm;
     }
-    ltot = ltot * w0 + l1 * w1;
-    m = mm;
-    if (grp == 1) return;
-  }
 
-  // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
-  if (qi <= last_row) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    uint16_t* optr = p.o + ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D;
+    // ---- epilogue: normalise, write O (bf16) and LSE (natural log).  The
+    // wave's 32 O rows pass through LDS (its own 32-row slice of the first
+    // slot of the K buffers, chunks XOR-swizzled by row as the tiles are) so
+    // that every global store writes whole rows.
+    {
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      const uint32_t ln = (uint32_t)lane;
+      const uint32_t ecol = ln & 31u, ehalf = ln >> 5;
+      unsigned char* stage = (wave < 2 ? &k_lds0[0][0] : &k_lds1[0][0]) + (wave & 1) * 32 * RB;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dim = 32 * db + 8 * r4 + 4 * half;
-        u32x2_t w;
-        w[0] = pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(optr + dim) = w;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          u32x2_t w;
+          w[0] = pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
+          w[1] = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+          const uint32_t c = (uint32_t)(4 * db + r4) ^ chunk_swz<D>(ecol);
+          *reinterpret_cast<u32x2_t*>(stage + ecol * RB + c * 16 + 8 * ehalf) = w;
+        }
+      // the wave reads back what its own lanes wrote: LDS operations of one
+      // wave complete in order once counted down
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+      for (int x = 0; x < 32 / RPI; ++x) {
+        const int r = x * RPI + (int)(ln / CPR);
+        const uint32_t c = (ln % CPR) ^ chunk_swz<D>((uint32_t)r);
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stage + r * RB + c * 16);
+        if (iw + r <= last_row)
+          *reinterpret_cast<u32x4_t*>(p.o + ((size_t)b * p.l_q + iw + r) * q_row +
+                                      (size_t)hq * D + 8 * (ln % CPR)) = val;
       }
-    if (half == 0) {
-      const float muse = (m == kNegInf) ? 0.f : m;
-      p.lse[(size_t)head * p.l_q + qi] =
-          ltot > 0.f ? (muse + __log2f(ltot)) * kLn2 : kNegInf;
+      if (half == 0 && qi <= last_row) {
+        const float muse = (m == kNegInf) ? 0.f : m;
+        p.lse[(size_t)head * p.l_q + qi] =
+            ltot > 0.f ? (muse + __log2f(ltot)) * kLn2 : kNegInf;
+      }
     }
+  };
+
+  int unit, head;
+  map_block(p, unit, head);
+  // pairing: the longer tile n_qtiles-1-r first, then r (once if the same)
+  const int n_tiles = p.pairs ? (unit == p.n_qtiles - 1 - unit ? 1 : 2) : 1;
+  for (int ti = 0; ti < n_tiles; ++ti) {
+    const int tile = p.pairs ? (ti == 0 ? p.n_qtiles - 1 - unit : unit) : unit;
+    // the previous tile's merge and output staging read LDS buffers that
+    // this tile's first loads overwrite
+    if (ti > 0) __syncthreads();
+    fwd_tile(tile, head);
   }
 }
 
@@ -570,6 +610,52 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdF32Params p) {
   }
 }
 
+// Workgroup schedule of the bf16 kernel:
+//  * kOneGroup: one q tile per 4-wave workgroup, two workgroups per CU;
+//  * kSplit: one q tile per 8-wave workgroup whose two key groups share the
+//    tile's keys, one workgroup per CU (half the time per tile);
+//  * kPairs: as kSplit, each workgroup taking q tiles n_qtiles-1-r and r.
+// The choice minimises an estimate of the makespan in units of one tile's
+// time on one 4-wave slot: max(longest workgroup, total work / slots).  The
+// 8-wave workgroup is charged 8% more per tile (its eight waves meet at every
+// barrier, so the MFMA and VALU phases of the two waves on a SIMD overlap
+// less than those of two independent workgroups).
+enum class FwdSchedule { kOneGroup, kSplit, kPairs };
+
+constexpr int kCUs = 256;
+
+int key_tiles(const FwdParams& p, int tile) {
+  const long long i0 = (long long)tile * kBM;
+  const long long jlo = std::max(0LL, i0 + p.dlo);
+  const long long jhi = std::min((long long)p.l_k - 1,
+                                 std::min(i0 + kBM - 1, (long long)p.l_q - 1) + p.dhi);
+  return jlo <= jhi ? (int)(jhi / 64 - jlo / 64 + 1) : 0;
+}
+
+FwdSchedule pick_schedule(const FwdParams& p) {
+  const int nt = p.n_qtiles;
+  long long max1 = 0, sum1 = 0, max2 = 0, sum2 = 0, maxp = 0, sump = 0;
+  for (int t = 0; t < nt; ++t) {
+    const long long len = key_tiles(p, t);
+    max1 = std::max(max1, len);
+    sum1 += len;
+    max2 = std::max(max2, (len + 1) / 2);
+    sum2 += (len + 1) / 2;
+  }
+  for (int r = 0; r < (nt + 1) / 2; ++r) {
+    const int a = nt - 1 - r;
+    const long long len = (key_tiles(p, a) + 1) / 2 + (a != r ? (key_tiles(p, r) + 1) / 2 : 0);
+    maxp = std::max(maxp, len);
+    sump += len;
+  }
+  const double heads = p.n_heads;
+  const double e1 = std::max((double)max1, sum1 * heads / (2.0 * kCUs));
+  const double e2 = 1.08 * std::max((double)max2, sum2 * heads / kCUs);
+  const double ep = 1.08 * std::max((double)maxp, sump * heads / kCUs);
+  if (ep < e1 && ep <= e2) return FwdSchedule::kPairs;
+  return e2 < e1 ? FwdSchedule::kSplit : FwdSchedule::kOneGroup;
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
@@ -595,11 +681,11 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
   p.q_xor = s.scale < 0.f ? 0x80008000u : 0u;
   p.dlo = s.dlo;
   p.dhi = s.dhi;
-  dim3 grid((unsigned)p.n_qtiles * (unsigned)p.n_heads);
-  // With no more workgroups than CUs (256), two per CU cannot fill the chip:
-  // split each q tile's keys over two groups of a workgroup instead.
-  const bool split = (long long)p.n_qtiles * p.n_heads <= 256;
-  if (split) {
+  const FwdSchedule sch = pick_schedule(p);
+  p.pairs = sch == FwdSchedule::kPairs ? 1 : 0;
+  p.n_units = p.pairs ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+  dim3 grid((unsigned)p.n_units * (unsigned)p.n_heads);
+  if (sch != FwdSchedule::kOneGroup) {
     if (s.d == 128)
       hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 2>), grid, dim3(2 * kThreads), 0, stream, p);
     else
