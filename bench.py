@@ -194,7 +194,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": counted_traffic(),
-                     "kernel": "fwd_bf16_kernel<128,64>",
+                     "kernel": "fwd_bf16_kernel<128, 64, 2>",
                      "kernel_ms_per_launch": round(kern_ms, 5),
                      "algorithmic_bytes": fwd_bytes(w.n, w.l_q, w.l_k, w.h,
                                                     w.h_kv, w.d, 2)},
