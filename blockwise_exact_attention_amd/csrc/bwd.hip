@@ -17,13 +17,16 @@
 //    through LDS.  S = Q K^T and dP = dO V^T come out with one key per lane,
 //    which is exactly the B-operand layout dV^T += dO^T P and
 //    dK^T += Q^T dS need, so P and dS never leave registers; dO^T and Q^T are
-//    staged transposed in LDS.
+//    read transposed out of the row-major tiles.
 //  * bwd_dq: one workgroup per 128 query rows of one head, Q and dO resident
 //    (B operands); key tiles stream through LDS.  S^T = K Q^T and
 //    dP^T = V dO^T put one query per lane, so dQ^T += K^T dS^T reads dS^T
-//    straight from registers; K^T is staged transposed in LDS.
+//    straight from registers; K^T is read transposed out of the K tile.
+// Tiles use the layout of the forward kernel (swizzled rows, direct loads,
+// two buffers one tile ahead).
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile.hpp"
 
 namespace bea {
 namespace {
@@ -47,51 +50,6 @@ struct BwdParams {
   float scale;
   int dlo, dhi;
 };
-
-// Position of row rr inside a transposed LDS row: the same in-16 permutation
-// as the forward's V^T (bits 2 and 3 swap), so a lane of half h reads its 8
-// k-slots {4h+0..3, 8+4h+0..3} as one 16-byte access.
-__device__ __forceinline__ int tr_pos(int rr) {
-  return (rr & ~12) | ((rr & 4) << 1) | ((rr & 8) >> 1);
-}
-
-// Copy a [ROWS x D] bf16 tile (row r at base + (r0 + r) * stride, rows
-// clamped to limit - 1) into LDS: row-major with row stride D + 8 when RM,
-// and transposed (dim-major, rows permuted by tr_pos, row stride ROWS + 8)
-// when TR.  Each thread moves groups of 4 rows x 8 dims.
-template <int ROWS, int D, bool RM, bool TR>
-__device__ __forceinline__ void tile_to_lds(const uint16_t* base, size_t stride,
-                                            int r0, int limit, uint16_t* rm,
-                                            uint16_t* tr) {
-  constexpr int GROUPS = (ROWS / 4) * (D / 8);
-  for (int gi = threadIdx.x; gi < GROUPS; gi += kThreads) {
-    const int rg = gi / (D / 8);
-    const int c8 = gi - rg * (D / 8);
-    u32x4_t x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = min(r0 + 4 * rg + r, limit - 1);
-      x[r] = *reinterpret_cast<const u32x4_t*>(base + (size_t)row * stride + c8 * 8);
-    }
-    if (RM) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<u32x4_t*>(&rm[(4 * rg + r) * (D + 8) + c8 * 8]) = x[r];
-    }
-    if (TR) {
-      const int pos = tr_pos(4 * rg);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        const int sh = (dd & 1) * 16;
-        u32x2_t pk;
-        pk[0] = ((x[0][w] >> sh) & 0xffffu) | (((x[1][w] >> sh) & 0xffffu) << 16);
-        pk[1] = ((x[2][w] >> sh) & 0xffffu) | (((x[3][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2_t*>(&tr[(c8 * 8 + dd) * (ROWS + 8) + pos]) = pk;
-      }
-    }
-  }
-}
 
 // ------------------------------------------------------------ preprocess
 
@@ -129,36 +87,41 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ dK, dV
+//
+// One workgroup per 128 keys of one key/value head, 4 waves x 32 keys; the
+// wave's K and V rows stay in VGPRs as B operands.  For every query head of
+// the group, tiles of 64 query rows of Q and dO stream through LDS (swizzled
+// rows, two buffers, loaded one tile ahead by direct buffer loads) with their
+// LSE * log2(e) and D entries.  Per tile: S = Q K^T and dP = dO V^T (Q and dO
+// rows as A operands) come out with one key per lane and one query per
+// k-slot position, which is the B layout of dV^T += dO^T P and
+// dK^T += Q^T dS, so P and dS stay in registers; dO^T and Q^T are read
+// transposed out of the row-major tiles.
 
 constexpr int kKeysPerWave = 32;
 constexpr int kKeysPerWG = 4 * kKeysPerWave;
 
 template <int D>
-struct __attribute__((aligned(16))) DkdvSmem {
-  static constexpr int BQ = 8192 / D;  // query rows per step (64 or 128)
-  uint16_t q[BQ * (D + 8)];
-  uint16_t qt[D * (BQ + 8)];
-  uint16_t dout[BQ * (D + 8)];
-  uint16_t doutt[D * (BQ + 8)];
-  float lse2[BQ];
-  float dd[BQ];
-};
-
-template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int n_ktiles,
                                                                int reverse) {
-  constexpr int BQ = DkdvSmem<D>::BQ;
+  constexpr int BQ = 64;         // query rows per tile
+  constexpr int RB = D * 2;      // bytes per tile row
+  constexpr int TB = BQ * RB;    // bytes per tile
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NQB = BQ / 32;
   constexpr int NPS = BQ / 16;
-  constexpr int RS = D + 8;
-  constexpr int TS = BQ + 8;
-  __shared__ DkdvSmem<D> sm;
+  constexpr uint32_t kVC = D == 128 ? 32u : 16u;
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char o_lds0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char o_lds1[TB];
+  __shared__ __attribute__((aligned(16))) float l_lds0[2 * BQ];  // LSE2 then D
+  __shared__ __attribute__((aligned(16))) float l_lds1[2 * BQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -177,6 +140,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
 
   const size_t kv_row = (size_t)p.h_kv * D;
   const size_t q_row = (size_t)p.h * D;
+  const uint32_t q_row_b = (uint32_t)q_row * 2u;
   // resident K and V rows of the wave's 32 keys
   u32x4_t kf[NDS], vf[NDS];
   {
@@ -204,141 +168,188 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
   const bool wave_live = kw <= last_key;
   const int kw_last = min(kw + kKeysPerWave - 1, last_key);
 
-  if (qlo <= qhi) {
-    const int t_begin = (int)(qlo / BQ);
-    const int t_end = (int)(qhi / BQ) + 1;
-    for (int hq = g * p.grp; hq < (g + 1) * p.grp; ++hq) {
-      const size_t rowbase = (size_t)b * p.l_q * q_row + (size_t)hq * D;
-      const size_t lbase = ((size_t)b * p.h + hq) * p.l_q;
-      for (int t = t_begin; t < t_end; ++t) {
-        const int i0 = t * BQ;
-        __syncthreads();
-        tile_to_lds<BQ, D, true, true>(p.q + rowbase, q_row, i0, p.l_q, sm.q, sm.qt);
-        tile_to_lds<BQ, D, true, true>(p.dout + rowbase, q_row, i0, p.l_q, sm.dout,
-                                       sm.doutt);
-        if (tid < BQ) {
-          const int i = min(i0 + tid, p.l_q - 1);
-          sm.lse2[tid] = p.lse2[lbase + i];
-          sm.dd[tid] = p.dd[lbase + i];
-        }
-        __syncthreads();
-        const int i_last = min(i0 + BQ - 1, p.l_q - 1);
-        const bool live = wave_live && (long long)kw_last - i0 >= p.dlo &&
-                          (long long)kw - i_last <= p.dhi;
-        if (!live) continue;
-        const bool full = (i0 + BQ <= p.l_q) && (kw + kKeysPerWave <= p.l_k) &&
-                          ((long long)kw - (i0 + BQ - 1) >= p.dlo) &&
-                          ((long long)(kw + kKeysPerWave - 1) - i0 <= p.dhi);
-        // S = Q K^T and dP = dO V^T: [32 queries x 32 keys] blocks, lane = key
-        f32x16_t sa[NQB], dpa[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            sa[qb][r] = 0.f;
-            dpa[qb][r] = 0.f;
-          }
-#pragma unroll
-          for (int s = 0; s < NDS; ++s) {
-            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-                &sm.q[(32 * qb + col) * RS + 16 * s + 8 * half]);
-            sa[qb] = mfma32x32x16(a, kf[s], sa[qb]);
-            const u32x4_t a2 = *reinterpret_cast<const u32x4_t*>(
-                &sm.dout[(32 * qb + col) * RS + 16 * s + 8 * half]);
-            dpa[qb] = mfma32x32x16(a2, vf[s], dpa[qb]);
-          }
-        }
-        // P = exp2(c s - lse2), dS = P (dP - D); both packed to bf16
-        u32x4_t pp[NPS], dsp[NPS];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int qi_loc = 32 * qb + 8 * r4 + 4 * half;
-            const f32x4_t l2 = *reinterpret_cast<const f32x4_t*>(&sm.lse2[qi_loc]);
-            const f32x4_t dv = *reinterpret_cast<const f32x4_t*>(&sm.dd[qi_loc]);
-            float pv[4], dsv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * r4 + e;
-              float pe = __builtin_amdgcn_exp2f(fmaf(sa[qb][r], p.c, -l2[e]));
-              if (!full) {
-                const int i = i0 + qi_loc + e;
-                const int rel = kj - i;
-                const bool ok = rel >= p.dlo && rel <= p.dhi && i < p.l_q &&
-                                kj < p.l_k;
-                pe = ok ? pe : 0.f;
-              }
-              pv[e] = pe;
-              dsv[e] = pe * (dpa[qb][r] - dv[e]);
-            }
-            const int t16 = 2 * qb + (r4 >> 1);
-            const int w0 = (r4 & 1) * 2;
-            pp[t16][w0] = pack_bf16x2(pv[0], pv[1]);
-            pp[t16][w0 + 1] = pack_bf16x2(pv[2], pv[3]);
-            dsp[t16][w0] = pack_bf16x2(dsv[0], dsv[1]);
-            dsp[t16][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
-          }
-        // dV^T += dO^T P ; dK^T += Q^T dS   (k-slots = query rows)
-#pragma unroll
-        for (int t16 = 0; t16 < NPS; ++t16)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(
-                &sm.doutt[(32 * db + col) * TS + 16 * t16 + 8 * half]);
-            dvt[db] = mfma32x32x16(ad, pp[t16], dvt[db]);
-            const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(
-                &sm.qt[(32 * db + col) * TS + 16 * t16 + 8 * half]);
-            dkt[db] = mfma32x32x16(aq, dsp[t16], dkt[db]);
-          }
-      }
+  const uint32_t lane_off = tile_lane_offset<D>(wave, lane, q_row_b);
+  uint32_t ka0, va0;
+  lds_read_bases<D>(lane, ka0, va0);
+
+  // steps u = (query head of the group, query tile) flattened
+  const int t_begin = qlo <= qhi ? (int)(qlo / BQ) : 0;
+  const int nt = qlo <= qhi ? (int)(qhi / BQ) + 1 - t_begin : 0;
+  const int n_steps = nt * p.grp;
+  auto load = [&](int u, unsigned char* qd, unsigned char* od, float* ld) {
+    const int hq = g * p.grp + u / nt;
+    const int i0 = (t_begin + u % nt) * BQ;
+    const size_t rowbase = (size_t)b * p.l_q * q_row + (size_t)hq * D;
+    tile_dma<D>(p.q + rowbase, i0, (long long)p.l_q - i0, q_row_b, qd, wave, lane_off);
+    tile_dma<D>(p.dout + rowbase, i0, (long long)p.l_q - i0, q_row_b, od, wave, lane_off);
+    if (wave < 2) {
+      // wave 0: LSE2 of the 64 rows, wave 1: D (rows past l_q read as 0)
+      const float* src = (wave == 0 ? p.lse2 : p.dd) + ((size_t)b * p.h + hq) * p.l_q + i0;
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(src), (short)0, (int)(4 * max(0, min(BQ, p.l_q - i0))), 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(ld + wave * BQ), 4,
+                                               (uint32_t)lane * 4u, 0, 0, 0);
     }
+  };
+  auto step = [&](int u, const unsigned char* ql, const unsigned char* ol, const float* ll,
+                  unsigned char* qn, unsigned char* on, float* ln) {
+    if (u + 1 < n_steps) load(u + 1, qn, on, ln);
+    const int i0 = (t_begin + u % nt) * BQ;
+    const int i_last = min(i0 + BQ - 1, p.l_q - 1);
+    const bool live = wave_live && (long long)kw_last - i0 >= p.dlo &&
+                      (long long)kw - i_last <= p.dhi;
+    if (live) {
+      const bool full = (i0 + BQ <= p.l_q) && (kw + kKeysPerWave <= p.l_k) &&
+                        ((long long)kw - (i0 + BQ - 1) >= p.dlo) &&
+                        ((long long)(kw + kKeysPerWave - 1) - i0 <= p.dhi);
+      uint32_t ka = ka0, va = va0;
+      asm volatile("" : "+v"(ka), "+v"(va));
+      // S = Q K^T and dP = dO V^T: [32 queries x 32 keys] blocks, lane = key
+      f32x16_t sa[NQB], dpa[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ql + qb * 32 * RB + (ka ^ (32u * s)));
+          sa[qb] = mfma32x32x16(a, kf[s], s == 0 ? f32x16_t{} : sa[qb]);
+          const u32x4_t a2 = *reinterpret_cast<const u32x4_t*>(ol + qb * 32 * RB + (ka ^ (32u * s)));
+          dpa[qb] = mfma32x32x16(a2, vf[s], s == 0 ? f32x16_t{} : dpa[qb]);
+        }
+      // P = exp2(c s - lse2), dS = P (dP - D); both packed to bf16
+      u32x4_t pp[NPS], dsp[NPS];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qi_loc = 32 * qb + 8 * r4 + 4 * half;
+          const f32x4_t l2 = *reinterpret_cast<const f32x4_t*>(ll + qi_loc);
+          const f32x4_t dv = *reinterpret_cast<const f32x4_t*>(ll + BQ + qi_loc);
+          float pv[4], dsv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float pe = __builtin_amdgcn_exp2f(fmaf(sa[qb][r], p.c, -l2[e]));
+            if (!full) {
+              const int i = i0 + qi_loc + e;
+              const int rel = kj - i;
+              const bool ok = (rel >= p.dlo) & (rel <= p.dhi) & (i < p.l_q) & (kj < p.l_k);
+              pe = ok ? pe : 0.f;
+            }
+            pv[e] = pe;
+            dsv[e] = pe * (dpa[qb][r] - dv[e]);
+          }
+          const int t16 = 2 * qb + (r4 >> 1);
+          const int w0 = (r4 & 1) * 2;
+          pp[t16][w0] = pack_bf16x2(pv[0], pv[1]);
+          pp[t16][w0 + 1] = pack_bf16x2(pv[2], pv[3]);
+          dsp[t16][w0] = pack_bf16x2(dsv[0], dsv[1]);
+          dsp[t16][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        }
+      // dV^T += dO^T P ; dK^T += Q^T dS   (k-slots = query rows)
+#pragma unroll
+      for (int t = 0; t < NPS; ++t)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const s16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(ol + t * 16 * RB + (va ^ (64u * db))));
+          const s16x4_t dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(ol + t * 16 * RB + 8 * RB + (va ^ (64u * db + kVC))));
+          const u32x2_t d2 = __builtin_bit_cast(u32x2_t, dlo);
+          const u32x2_t d3 = __builtin_bit_cast(u32x2_t, dhi);
+          dvt[db] = mfma32x32x16(u32x4_t{d2[0], d2[1], d3[0], d3[1]}, pp[t], dvt[db]);
+          const s16x4_t qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(ql + t * 16 * RB + (va ^ (64u * db))));
+          const s16x4_t qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(ql + t * 16 * RB + 8 * RB + (va ^ (64u * db + kVC))));
+          const u32x2_t q2 = __builtin_bit_cast(u32x2_t, qlo);
+          const u32x2_t q3 = __builtin_bit_cast(u32x2_t, qhi);
+          dkt[db] = mfma32x32x16(u32x4_t{q2[0], q2[1], q3[0], q3[1]}, dsp[t], dkt[db]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads landed
+    __syncthreads();
+  };
+  if (n_steps > 0) {
+    load(0, q_lds0, o_lds0, l_lds0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+  // unrolled by two so that every buffer reference is a fixed LDS object
+  for (int u = 0; u < n_steps; u += 2) {
+    step(u, q_lds0, o_lds0, l_lds0, q_lds1, o_lds1, l_lds1);
+    if (u + 1 < n_steps) step(u + 1, q_lds1, o_lds1, l_lds1, q_lds0, o_lds0, l_lds0);
   }
 
-  if (kj <= last_key) {
-    const size_t off = ((size_t)b * p.l_k + kj) * kv_row + (size_t)g * D;
+  // ---- epilogue: dK = scale dK^T, dV = dV^T as bf16, 32 key rows per wave
+  // staged through LDS (dK rows in the Q buffers, dV rows in the dO buffers,
+  // swizzled like the tiles) so that every store writes whole rows
+  uint32_t ln = (uint32_t)lane;
+  asm volatile("" : "+v"(ln));
+  const uint32_t ecol = ln & 31u, ehalf = ln >> 5;
+  unsigned char* stk = (wave < 2 ? q_lds0 : q_lds1) + (wave & 1) * 32 * RB;
+  unsigned char* stv = (wave < 2 ? o_lds0 : o_lds1) + (wave & 1) * 32 * RB;
+  static_assert(2 * 32 * RB <= TB, "staging fits");
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dim = 32 * db + 8 * r4 + 4 * half;
-        u32x2_t wk, wv;
-        wk[0] = pack_bf16x2(dkt[db][4 * r4] * p.scale, dkt[db][4 * r4 + 1] * p.scale);
-        wk[1] = pack_bf16x2(dkt[db][4 * r4 + 2] * p.scale, dkt[db][4 * r4 + 3] * p.scale);
-        wv[0] = pack_bf16x2(dvt[db][4 * r4], dvt[db][4 * r4 + 1]);
-        wv[1] = pack_bf16x2(dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]);
-        *reinterpret_cast<u32x2_t*>(p.dk + off + dim) = wk;
-        *reinterpret_cast<u32x2_t*>(p.dv + off + dim) = wv;
-      }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      u32x2_t wk, wv;
+      wk[0] = pack_bf16x2(dkt[db][4 * r4] * p.scale, dkt[db][4 * r4 + 1] * p.scale);
+      wk[1] = pack_bf16x2(dkt[db][4 * r4 + 2] * p.scale, dkt[db][4 * r4 + 3] * p.scale);
+      wv[0] = pack_bf16x2(dvt[db][4 * r4], dvt[db][4 * r4 + 1]);
+      wv[1] = pack_bf16x2(dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]);
+      const uint32_t c = (uint32_t)(4 * db + r4) ^ chunk_swz<D>(ecol);
+      *reinterpret_cast<u32x2_t*>(stk + ecol * RB + c * 16 + 8 * ehalf) = wk;
+      *reinterpret_cast<u32x2_t*>(stv + ecol * RB + c * 16 + 8 * ehalf) = wv;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int x = 0; x < 32 / RPI; ++x) {
+    const int r = x * RPI + (int)(ln / CPR);
+    const uint32_t c = (ln % CPR) ^ chunk_swz<D>((uint32_t)r);
+    const u32x4_t vk = *reinterpret_cast<const u32x4_t*>(stk + r * RB + c * 16);
+    const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(stv + r * RB + c * 16);
+    if (kw + r <= last_key) {
+      const size_t off = ((size_t)b * p.l_k + kw + r) * kv_row + (size_t)g * D + 8 * (ln % CPR);
+      *reinterpret_cast<u32x4_t*>(p.dk + off) = vk;
+      *reinterpret_cast<u32x4_t*>(p.dv + off) = vv;
+    }
   }
 }
 
 // ------------------------------------------------------------ dQ
+//
+// One workgroup per 128 query rows of one head, 4 waves x 32 rows; the
+// wave's Q and dO rows stay in VGPRs as B operands, its LSE and D per lane.
+// Key tiles of 64 rows of K and V stream through LDS (swizzled rows, two
+// buffers, one tile ahead, direct buffer loads).  Per tile: S^T = K Q^T and
+// dP^T = V dO^T (K and V rows as A operands) put one query per lane;
+// P^T = exp2(c S^T - LSE2), dS^T = P^T (dP^T - D), and dQ^T += K^T dS^T with
+// K^T read transposed out of the row-major K tile reads dS^T straight from
+// registers as its B operand.
 
 template <int D>
-struct __attribute__((aligned(16))) DqSmem {
-  static constexpr int BN = 8192 / D;  // keys per step (64 or 128)
-  uint16_t k[BN * (D + 8)];
-  uint16_t kt[D * (BN + 8)];
-  uint16_t v[BN * (D + 8)];
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p, int n_qtiles,
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_qtiles,
                                                              int reverse) {
-  constexpr int BN = DqSmem<D>::BN;
+  constexpr int BN = 64;
+  constexpr int RB = D * 2;
+  constexpr int TB = BN * RB;
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NKB = BN / 32;
   constexpr int NPS = BN / 16;
-  constexpr int RS = D + 8;
-  constexpr int TS = BN + 8;
   constexpr int BM = 128;
-  __shared__ DqSmem<D> sm;
+  constexpr uint32_t kVC = D == 128 ? 32u : 16u;
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -356,6 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p, int n_
 
   const size_t q_row = (size_t)p.h * D;
   const size_t kv_row = (size_t)p.h_kv * D;
+  const uint32_t kv_row_b = (uint32_t)kv_row * 2u;
   u32x4_t qf[NDS], dof[NDS];
   {
     const size_t off = ((size_t)b * p.l_q + min(qi, last_row)) * q_row +
@@ -387,38 +399,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p, int n_
   const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
   const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
 
+  const uint32_t lane_off = tile_lane_offset<D>(wave, lane, kv_row_b);
+  uint32_t ka0, va0;
+  lds_read_bases<D>(lane, ka0, va0);
+  auto load = [&](int kt, unsigned char* kd, unsigned char* vd) {
+    const long long j0 = (long long)kt * BN;
+    tile_dma<D>(kbase, j0, (long long)p.l_k - j0, kv_row_b, kd, wave, lane_off);
+    tile_dma<D>(vbase, j0, (long long)p.l_k - j0, kv_row_b, vd, wave, lane_off);
+  };
+
+  int kt_begin = 0, kt_end = 0;
   if (jlo <= jhi) {
-    const int kt_begin = (int)(jlo / BN);
-    const int kt_end = (int)(jhi / BN) + 1;
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const int j0 = kt * BN;
-      __syncthreads();
-      tile_to_lds<BN, D, true, true>(kbase, kv_row, j0, p.l_k, sm.k, sm.kt);
-      tile_to_lds<BN, D, true, false>(vbase, kv_row, j0, p.l_k, sm.v, nullptr);
-      __syncthreads();
-      const bool live = wave_live && (long long)j0 <= wjhi &&
-                        (long long)(j0 + BN - 1) >= wjlo;
-      if (!live) continue;
+    kt_begin = (int)(jlo / BN);
+    kt_end = (int)(jhi / BN) + 1;
+  }
+  auto step = [&](int kt, const unsigned char* kl, const unsigned char* vl, unsigned char* kn,
+                  unsigned char* vn) {
+    if (kt + 1 < kt_end) load(kt + 1, kn, vn);
+    const int j0 = kt * BN;
+    const bool live = wave_live && (long long)j0 <= wjhi && (long long)(j0 + BN - 1) >= wjlo;
+    if (live) {
       const bool full = (j0 + BN <= p.l_k) && ((long long)j0 - wb >= p.dlo) &&
                         ((long long)(j0 + BN - 1) - wa <= p.dhi);
+      uint32_t ka = ka0, va = va0;
+      asm volatile("" : "+v"(ka), "+v"(va));
+      // S^T = K Q^T and dP^T = V dO^T: lane = query
       f32x16_t sa[NKB], dpa[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sa[kb][r] = 0.f;
-          dpa[kb][r] = 0.f;
-        }
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int s = 0; s < NDS; ++s) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              &sm.k[(32 * kb + col) * RS + 16 * s + 8 * half]);
-          sa[kb] = mfma32x32x16(a, qf[s], sa[kb]);
-          const u32x4_t a2 = *reinterpret_cast<const u32x4_t*>(
-              &sm.v[(32 * kb + col) * RS + 16 * s + 8 * half]);
-          dpa[kb] = mfma32x32x16(a2, dof[s], dpa[kb]);
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * RB + (ka ^ (32u * s)));
+          sa[kb] = mfma32x32x16(a, qf[s], s == 0 ? f32x16_t{} : sa[kb]);
+          const u32x4_t a2 = *reinterpret_cast<const u32x4_t*>(vl + kb * 32 * RB + (ka ^ (32u * s)));
+          dpa[kb] = mfma32x32x16(a2, dof[s], s == 0 ? f32x16_t{} : dpa[kb]);
         }
-      }
       u32x4_t dsp[NPS];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -431,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p, int n_
             if (!full) {
               const int j = j0 + 32 * kb + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
               const int rel = j - qi;
-              const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
+              const bool ok = (rel >= p.dlo) & (rel <= p.dhi) & (j < p.l_k);
               pe = ok ? pe : 0.f;
             }
             ds2[e] = pe * (dpa[kb][r + e] - dval);
@@ -440,28 +455,61 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p, int n_
         }
       // dQ^T += K^T dS^T   (k-slots = keys)
 #pragma unroll
-      for (int t16 = 0; t16 < NPS; ++t16)
+      for (int t = 0; t < NPS; ++t)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              &sm.kt[(32 * db + col) * TS + 16 * t16 + 8 * half]);
-          dqt[db] = mfma32x32x16(a, dsp[t16], dqt[db]);
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(kl + t * 16 * RB + (va ^ (64u * db))));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(kl + t * 16 * RB + 8 * RB + (va ^ (64u * db + kVC))));
+          const u32x2_t l2v = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t h2v = __builtin_bit_cast(u32x2_t, hi);
+          dqt[db] = mfma32x32x16(u32x4_t{l2v[0], l2v[1], h2v[0], h2v[1]}, dsp[t], dqt[db]);
         }
     }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads landed
+    __syncthreads();
+  };
+  if (kt_begin < kt_end) {
+    load(kt_begin, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+  // unrolled by two so that every buffer reference is a fixed LDS object
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
+    step(kt, k_lds0, v_lds0, k_lds1, v_lds1);
+    if (kt + 1 < kt_end) step(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
-  if (qi <= last_row) {
-    uint16_t* optr = p.dq + ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D;
+  // ---- epilogue: dQ = scale dQ^T as bf16, the wave's 32 rows staged
+  // through LDS (swizzled like the tiles) so that every store writes whole
+  // rows
+  uint32_t ln = (uint32_t)lane;
+  asm volatile("" : "+v"(ln));
+  const uint32_t ecol = ln & 31u, ehalf = ln >> 5;
+  unsigned char* stage = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * 32 * RB;
+  static_assert(2 * 32 * RB <= TB, "staging fits");
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dim = 32 * db + 8 * r4 + 4 * half;
-        u32x2_t w;
-        w[0] = pack_bf16x2(dqt[db][4 * r4] * p.scale, dqt[db][4 * r4 + 1] * p.scale);
-        w[1] = pack_bf16x2(dqt[db][4 * r4 + 2] * p.scale, dqt[db][4 * r4 + 3] * p.scale);
-        *reinterpret_cast<u32x2_t*>(optr + dim) = w;
-      }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      u32x2_t w;
+      w[0] = pack_bf16x2(dqt[db][4 * r4] * p.scale, dqt[db][4 * r4 + 1] * p.scale);
+      w[1] = pack_bf16x2(dqt[db][4 * r4 + 2] * p.scale, dqt[db][4 * r4 + 3] * p.scale);
+      const uint32_t c = (uint32_t)(4 * db + r4) ^ chunk_swz<D>(ecol);
+      *reinterpret_cast<u32x2_t*>(stage + ecol * RB + c * 16 + 8 * ehalf) = w;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;
+#pragma unroll
+  for (int x = 0; x < 32 / RPI; ++x) {
+    const int r = x * RPI + (int)(ln / CPR);
+    const uint32_t c = (ln % CPR) ^ chunk_swz<D>((uint32_t)r);
+    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stage + r * RB + c * 16);
+    if (iw + r <= last_row)
+      *reinterpret_cast<u32x4_t*>(p.dq + ((size_t)b * p.l_q + iw + r) * q_row +
+                                  (size_t)hq * D + 8 * (ln % CPR)) = val;
   }
 }
 

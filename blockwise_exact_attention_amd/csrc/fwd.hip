@@ -27,6 +27,7 @@
 //    writes whole rows rather than 16-byte pieces of 32 rows.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile.hpp"
 
 namespace bea {
 namespace {
@@ -103,52 +104,6 @@ __device__ __forceinline__ float pair_sum(float x) {
 // 2^8, exact in meaning (O = sum p v / sum p for any fixed shift) and far from
 // fp32 or bf16 range limits.
 constexpr float kRescaleSlack = 8.f;
-
-// Tiles move HBM -> LDS by buffer loads that write LDS directly (no VGPR
-// staging; rows past l_k arrive as zeros).  A tile is stored row-major with
-// unpadded rows whose 16-byte chunks are XOR-swizzled by row, which keeps
-// both readers free of bank conflicts: the S^T MFMA reads K rows as its A
-// operand, and the P.V MFMA reads V transposed with ds_read_b64_tr_b16 (each
-// 16-lane group gathers 4 keys x 4 dims and hands every lane one dim of the
-// 4 keys).
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
-
-// Chunk swizzle of row r.  D = 128 (16 chunks per row): 4 (r % 4) + (r / 4) % 4,
-// so 16 consecutive rows and 4 consecutive rows x 4 chunk pairs each cover
-// all 16 chunk positions.  D = 64 (8 chunks, two rows per 64 banks): the
-// 3-bit reversal of (r / 2) % 8.
-template <int D>
-__device__ __forceinline__ uint32_t chunk_swz(uint32_t r) {
-  if (D == 128) return ((r & 3u) << 2) | ((r >> 2) & 3u);
-  const uint32_t x = (r >> 1) & 7u;
-  return ((x & 1u) << 2) | (x & 2u) | ((x >> 2) & 1u);
-}
-
-
-// Per-lane LDS read addresses of the swizzled tiles.  The swizzle is an XOR
-// on chunk bits, so every address is one base XOR an immediate.
-//  * S^T A operand, slice s: row col (+ 32 kb), logical chunk 2 s + half:
-//      col * RB + 16 ((2 s + half) ^ swz(col)) = ka0 ^ (32 s).
-//  * P.V A operand, transposed read c of slice t for dim block db: the lane
-//    addresses key 16 t + 8 c + 4 h + m and dims 32 db + 16 (G % 2) + 4 a .. +3,
-//    with (G, a, m) = (lane / 16, lane % 4, (lane / 4) % 4) and h = G / 2:
-//      D = 128: key*256 + 16 ((4 db + 2 g2 + a/2) ^ (4 m + (2 c ^ h))) + 8 (a & 1)
-//             = 2048 c + (va0 ^ (64 db + 32 c)),  g2 = G % 2;
-//      D = 64:  key*128 + 16 ((4 db + 2 g2 + a/2) ^ (4 (m/2) + 2 h + c)) + 8 (a & 1)
-//             = 1024 c + (va0 ^ (64 db + 16 c)).
-template <int D>
-__device__ __forceinline__ void lds_read_bases(int lane, uint32_t& ka0, uint32_t& va0) {
-  constexpr uint32_t RB = D * 2;
-  const uint32_t col = (uint32_t)lane & 31u, half = (uint32_t)lane >> 5;
-  ka0 = col * RB | ((half ^ chunk_swz<D>(col)) * 16u);
-  const uint32_t G = (uint32_t)lane >> 4, a = (uint32_t)lane & 3u;
-  const uint32_t mm = ((uint32_t)lane >> 2) & 3u, hh = G >> 1, g2 = G & 1u;
-  const uint32_t z = D == 128 ? ((mm << 2) | ((2u * g2 + (a >> 1)) ^ hh))
-                              : (((mm >> 1) << 2) | ((g2 ^ hh) << 1) | (a >> 1));
-  va0 = (4u * hh + mm) * RB | (z * 16u) | ((a & 1u) * 8u);
-}
 
 // KSPLIT = 2: eight waves per workgroup in two groups of four that cover the
 // same 128 query rows and take alternate key tiles, each group with its own
