@@ -45,20 +45,20 @@ def parse():
 
 
 def timed(fn, steps, warmup, torch):
-    """Median/mean per-call time (ms) of fn() with events on the current
-    stream (the one every library call is launched on)."""
+    """Mean GPU time per call (ms) of fn(), called `steps` times back to back
+    between one event pair on the current stream (the one every library call
+    is launched on), so that the events' own cost is spread over the calls."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        a.record()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
         fn()
-        b.record()
+    b.record()
     torch.cuda.synchronize()
-    ts = np.array([a.elapsed_time(b) for a, b in ev])
-    return float(np.median(ts)), float(np.mean(ts))
+    return a.elapsed_time(b) / steps
 
 
 def cpu_baseline(x, w, seconds):
@@ -91,19 +91,30 @@ def cpu_baseline(x, w, seconds):
                       f"numpy, {dt:.1f} s"}
 
 
+KERNEL_SOURCES = ("fwd.hip", "tile.hpp", "common.hpp")
+
+
+def kernel_sources_sha256():
+    """sha256 over the forward kernel's source files, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "blockwise_exact_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def counted_traffic():
     """HBM bytes per forward launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or
-    None when the kernel source changed since the counters were taken."""
-    import hashlib
+    None when the kernel sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "fwd_bf16_causal_mha_n2_l2048_h16_d128_counters.json")
-    src = os.path.join(ROOT, "blockwise_exact_attention_amd", "csrc", "fwd.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_sources_sha256()
     except (OSError, ValueError):
         return None
-    if rec.get("fwd_hip_sha256") != sha:
+    if rec.get("kernel_sources_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -231,12 +242,12 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
             A.attn_fwd(tq, kc[s], vc[s], share.blk, share.lse_blk,
                        w.softmax_scale, True, -1, -1, x["q_offset"],
                        x["k_offsets"][s])
-        fwd_ms.append(timed(f, steps, 5, torch)[0])
+        fwd_ms.append(timed(f, steps, 5, torch))
     A.attn_acc_init(share.acc, share.lse_acc)
     merge_ms.append(timed(lambda: A.attn_merge(share.acc, share.lse_acc,
                                                share.blk, share.lse_blk),
-                          steps, 5, torch)[0])
-    e2e = timed(lambda: share.run(kc, vc, x["k_offsets"]), steps, 3, torch)[0]
+                          steps, 5, torch))
+    e2e = timed(lambda: share.run(kc, vc, x["k_offsets"]), steps, 3, torch)
     pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, 7168, 1024 * s)
                 for s in range(8))
     fl = fwd_flops(1, 32, 128, pairs)
@@ -256,7 +267,7 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
     o = torch.empty_like(tq)
     lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
     ms = timed(lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True,
-                                  w.win_l, w.win_r), steps, 5, torch)[0]
+                                  w.win_l, w.win_r), steps, 5, torch)
     pairs = allowed_pairs(w.l_q, w.l_k, True, w.win_l, w.win_r)
     fl = fwd_flops(w.n, w.h, w.d, pairs)
     res["window_256"] = {"ms": round(ms, 4),
@@ -270,7 +281,7 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
     o = torch.empty_like(tq)
     lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
     ms = timed(lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True),
-               max(5, steps // 4), 3, torch)[0]
+               max(5, steps // 4), 3, torch)
     pairs = allowed_pairs(w.l_q, w.l_k, True)
     res["long_16k"] = {"fwd_ms": round(ms, 4),
                        "fwd_tflops": round(fwd_flops(w.n, w.h, w.d, pairs)
@@ -282,7 +293,7 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
                          device=dev)
         msb = timed(lambda: A.attn_bwd(tdo, tq, tk, tv, o, lse, dq, dk, dv,
                                        w.softmax_scale, True, workspace=ws),
-                    max(5, steps // 8), 2, torch)[0]
+                    max(5, steps // 8), 2, torch)
         res["long_16k"]["bwd_ms"] = round(msb, 4)
         res["long_16k"]["bwd_tflops"] = round(
             bwd_flops(w.n, w.h, w.d, pairs) / (msb * 1e-3) / 1e12, 2)

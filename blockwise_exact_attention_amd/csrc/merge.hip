@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 constexpr int kMergeMaxRows = 256;
-constexpr int kMergeElems = 8192;  // elements per block on the vector path
+constexpr int kMergeElems = 2048;  // elements per block on the vector path
 constexpr int kMergeVec = kMergeElems / (4 * kMergeThreads);  // float4 per thread
 
 // Row weights: mode 0 keep the accumulator, 1 take the block, 2 weighted
@@ -54,7 +54,7 @@ __device__ __forceinline__ void merge_row_weights(float* __restrict__ lse_acc,
   }
 }
 
-// Vector path (d % 4 == 0, 8192 / d rows per block): a block covers
+// Vector path (d % 4 == 0, 2048 / d rows per block): a block covers
 // consecutive query rows i0 .. i0 + R - 1 of one (batch, head), so its LSE
 // reads are contiguous; its O rows are R rows h*d apart, each row contiguous.
 // Every thread issues its data loads (the block's values and, speculatively,
@@ -171,17 +171,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   }
 }
 
+// 16-byte stores where the accumulator is 16-byte aligned (n4 = n_acc / 4),
+// 4-byte stores for the rest.
 __global__ __launch_bounds__(256) void acc_init_kernel(float* __restrict__ acc,
                                                        float* __restrict__ lse,
                                                        long long n_acc,
+                                                       long long n4,
                                                        long long n_lse) {
   const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n_acc;
-       e += stride)
-    acc[e] = 0.f;
-  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n_lse;
-       e += stride)
-    lse[e] = kNegInf;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (long long e = t; e < n4; e += stride)
+    reinterpret_cast<f32x4_t*>(acc)[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (long long e = n4 * 4 + t; e < n_acc; e += stride) acc[e] = 0.f;
+  for (long long e = t; e < n_lse; e += stride) lse[e] = kNegInf;
 }
 
 template <bool BF16>
@@ -257,8 +259,9 @@ hipError_t launch_acc_init(float* out_acc, float* lse_acc, int n, int l, int h,
                            int d, hipStream_t stream) {
   const long long n_acc = (long long)n * l * h * d;
   const long long n_lse = (long long)n * l * h;
-  hipLaunchKernelGGL(acc_init_kernel, dim3(grid_for(n_acc, 256 * 4)), dim3(256),
-                     0, stream, out_acc, lse_acc, n_acc, n_lse);
+  const long long n4 = (reinterpret_cast<uintptr_t>(out_acc) % 16 == 0) ? n_acc / 4 : 0;
+  hipLaunchKernelGGL(acc_init_kernel, dim3(grid_for(n_acc / 4 + 1, 256)), dim3(256),
+                     0, stream, out_acc, lse_acc, n_acc, n4, n_lse);
   return hipGetLastError();
 }
 

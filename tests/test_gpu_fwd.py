@@ -186,7 +186,7 @@ def _partial(rng, n, l, h, d, p_empty):
     return o, lse
 
 
-@pytest.mark.parametrize("d", [128, 64, 5])
+@pytest.mark.parametrize("d", [128, 64, 256, 5])
 @pytest.mark.parametrize("blk_dtype", ["bf16", "f32"])
 def test_merge_parity(d, blk_dtype):
     rng = np.random.default_rng(d)
@@ -230,6 +230,16 @@ def test_acc_init_and_cast():
     A.attn_acc_cast(x, out32)
     torch.cuda.synchronize()
     assert torch.equal(out32, x)
+    # an accumulator 4 bytes past a 16-byte boundary, with a ragged size: the
+    # scalar stores cover it all and nothing beyond it
+    buf = torch.full((1 + 5 * 3 * 7 + 1,), 7.0, device="cuda")
+    acc_u = buf[1:-1].view(1, 5, 3, 7)
+    lse_u = torch.zeros((1, 3, 5), device="cuda")
+    A.attn_acc_init(acc_u, lse_u)
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.all(b[1:-1] == 0) and b[0] == 7.0 and b[-1] == 7.0
+    assert torch.all(torch.isneginf(lse_u))
 
 
 def test_small_ring_share_gqa():
