@@ -78,6 +78,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
   const size_t row_stride = (size_t)h * d;
   const size_t base = ((size_t)b * l + i0) * row_stride + (size_t)hq * d;
 
+  // the row's two LSE values first: their round trip decides the weights
+  float la = kNegInf, lb = kNegInf;
+  const size_t li = (size_t)bh * l + i0 + tid;
+  if (tid < nr) {
+    la = lse_acc[li];
+    lb = lse_blk[li];
+  }
   f32x4_t av[kMergeVec], bv[kMergeVec];
 #pragma unroll
   for (int v = 0; v < kMergeVec; ++v) {
@@ -96,9 +103,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
     }
   }
   if (tid < nr) {
-    const size_t li = (size_t)bh * l + i0 + tid;
-    const float a = lse_acc[li];
-    const float bb = lse_blk[li];
+    const float a = la;
+    const float bb = lb;
     int mode = 2;
     float wa = 0.f, wb = 0.f;
     if (bb == kNegInf) {
