@@ -205,7 +205,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": counted_traffic(),
-                     "kernel": "fwd_bf16_kernel<128, 64, 2>",
+                     "kernel": "fwd_bf16_kernel<128, 64, 2, false>",
                      "kernel_ms_per_launch": round(kern_ms, 5),
                      "algorithmic_bytes": fwd_bytes(w.n, w.l_q, w.l_k, w.h,
                                                     w.h_kv, w.d, 2)},
@@ -248,6 +248,8 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
                                                share.blk, share.lse_blk),
                           steps, 5, torch))
     e2e = timed(lambda: share.run(kc, vc, x["k_offsets"]), steps, 3, torch)
+    e2e_fused = timed(lambda: share.run(kc, vc, x["k_offsets"], fused=True),
+                      steps, 3, torch)
     pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, 7168, 1024 * s)
                 for s in range(8))
     fl = fwd_flops(1, 32, 128, pairs)
@@ -257,7 +259,9 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
         "fwd_ms_per_step": [round(v, 4) for v in fwd_ms],
         "merge_ms": round(merge_ms[0], 4),
         "merge_gbs_warm": round(mb / (merge_ms[0] * 1e-3) / 1e9, 1),
-        "end_to_end_ms": round(e2e, 4)}
+        "end_to_end_ms": round(e2e, 4),
+        "end_to_end_fused_ms": round(e2e_fused, 4),
+        "fused_tflops": round(fl / (e2e_fused * 1e-3) / 1e12, 2)}
     del share, kc, vc, tq
 
     # sliding window

@@ -29,6 +29,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                       _i, _i, _ll, _ll, _vp, _i]),
+    "attn_fwd_acc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                          _i, _i, _ll, _ll, _vp, _i]),
     "attn_merge": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_acc_init": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_acc_cast": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp]),

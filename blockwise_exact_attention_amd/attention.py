@@ -92,6 +92,31 @@ def attn_merge(out_acc, lse_acc, out_blk, lse_blk, stream=None):
     return out_acc, lse_acc
 
 
+def attn_fwd_acc(q, k, v, out_acc, lse_acc, scale, causal=False, win_l=-1,
+                 win_r=-1, q_offset=0, k_offset=0, stream=None):
+    """One fused ring step: attention of bf16 q against this k/v chunk merged
+    into the float32 accumulator (out_acc [n,l_q,h,d], lse_acc [n,h,l_q])."""
+    _dev(q, k, v, out_acc, lse_acc)
+    n, l_q, h, d = q.shape
+    _, l_k, h_kv, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != n or k.shape[3] != d:
+        raise ValueError("k and v must be [n, l_k, h_kv, d] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if out_acc.shape != q.shape or out_acc.dtype != torch.float32:
+        raise ValueError("out_acc must be float32 shaped like q")
+    if tuple(lse_acc.shape) != (n, h, l_q) or lse_acc.dtype != torch.float32:
+        raise ValueError("lse_acc must be float32 [n, h, l_q]")
+    st = _lib.lib().attn_fwd_acc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 out_acc.data_ptr(), lse_acc.data_ptr(), n, l_q,
+                                 l_k, h, h_kv, d, float(scale),
+                                 int(bool(causal)), int(win_l), int(win_r),
+                                 int(q_offset), int(k_offset), _stream(stream),
+                                 _dtype_code(q))
+    check("attn_fwd_acc", st)
+    return out_acc, lse_acc
+
+
 def attn_acc_init(out_acc, lse_acc, stream=None):
     _dev(out_acc, lse_acc)
     n, l, h, d = out_acc.shape
@@ -156,9 +181,10 @@ def attention_backward(dout, q, k, v, out, lse, scale=None, causal=False,
 class RingShare:
     """One device's share of ring attention, with its buffers allocated once:
     the float32 accumulator (O, LSE), one block (O, LSE) per step and the
-    final output.  `run` launches acc_init, then attn_fwd + attn_merge per
-    key/value chunk with that chunk's absolute offset, then the final cast -
-    all on one stream, nothing synchronised (flash_sharding.py, ring_fwd)."""
+    final output.  `run` launches acc_init, then per key/value chunk (with
+    that chunk's absolute offset) either attn_fwd + attn_merge or, with
+    fused=True, the single attn_fwd_acc step, then the final cast - all on
+    one stream, nothing synchronised (flash_sharding.py, ring_fwd)."""
 
     def __init__(self, q, scale, causal, q_offset):
         n, l, h, d = q.shape
@@ -173,19 +199,24 @@ class RingShare:
         self.lse_blk = torch.empty((n, h, l), dtype=torch.float32, device=dev)
         self.out = torch.empty_like(q)
 
-    def run(self, k_chunks, v_chunks, k_offsets, stream=None):
+    def run(self, k_chunks, v_chunks, k_offsets, stream=None, fused=False):
         attn_acc_init(self.acc, self.lse_acc, stream)
         for kc, vc, ko in zip(k_chunks, v_chunks, k_offsets):
-            attn_fwd(self.q, kc, vc, self.blk, self.lse_blk, self.scale,
-                     self.causal, -1, -1, self.q_offset, ko, stream)
-            attn_merge(self.acc, self.lse_acc, self.blk, self.lse_blk, stream)
+            if fused:
+                attn_fwd_acc(self.q, kc, vc, self.acc, self.lse_acc, self.scale,
+                             self.causal, -1, -1, self.q_offset, ko, stream)
+            else:
+                attn_fwd(self.q, kc, vc, self.blk, self.lse_blk, self.scale,
+                         self.causal, -1, -1, self.q_offset, ko, stream)
+                attn_merge(self.acc, self.lse_acc, self.blk, self.lse_blk,
+                           stream)
         attn_acc_cast(self.acc, self.out, stream)
         return self.out, self.lse_acc
 
 
 def ring_share(q, k_chunks, v_chunks, k_offsets, q_offset, scale=None,
-               causal=True, stream=None):
+               causal=True, stream=None, fused=False):
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     return RingShare(q, scale, causal, q_offset).run(k_chunks, v_chunks,
-                                                     k_offsets, stream)
+                                                     k_offsets, stream, fused)

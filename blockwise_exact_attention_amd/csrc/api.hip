@@ -115,6 +115,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                                    : bea::launch_fwd_f32(q, k, v, out, lse, s, hs));
 }
 
+int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
+                 float* lse_acc, int n, int l_q, int l_k, int h, int h_kv, int d,
+                 float scale, int causal, int win_l, int win_r,
+                 long long q_offset, long long k_offset, void* stream, int dtype) {
+  if (!q || !k || !v || !out_acc || !lse_acc) return ATTN_ERR_NULL;
+  int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(out_acc, 16) || !aligned(lse_acc, 4))
+    return ATTN_ERR_ALIGN;
+  const long long qb = (long long)n * l_q * h * d * 2;
+  const long long kb = (long long)n * l_k * h_kv * d * 2;
+  const long long ab = (long long)n * l_q * h * d * 4;
+  const long long lb = (long long)n * h * l_q * 4;
+  const Range rq = range(q, qb), rk = range(k, kb), rv = range(v, kb),
+              ra = range(out_acc, ab), rl = range(lse_acc, lb);
+  if (overlap(ra, rq) || overlap(ra, rk) || overlap(ra, rv) ||
+      overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ra))
+    return ATTN_ERR_ALIAS;
+
+  AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+  mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
+  (void)hipGetLastError();
+  return finish(bea::launch_fwd_bf16(q, k, v, nullptr, nullptr, s,
+                                     static_cast<hipStream_t>(stream), out_acc,
+                                     lse_acc));
+}
+
 int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
                const float* lse_blk, int n, int l, int h, int d, int blk_dtype,
                void* stream) {

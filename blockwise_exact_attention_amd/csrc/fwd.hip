@@ -42,6 +42,8 @@ struct FwdParams {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
+  float* acc;      // ACC kernels: fp32 accumulator O [n, l_q, h, d] (else unused)
+  float* lse_acc;  // ACC kernels: its LSE [n, h, l_q] (natural log)
   int l_q, l_k, h, h_kv, grp;
   int n_heads;     // n * h
   int n_qtiles;
@@ -112,7 +114,11 @@ constexpr float kRescaleSlack = 8.f;
 // time with one workgroup per CU, which lets a small or causal-imbalanced
 // grid run longest-first and balance.  Under pairing a workgroup takes two q
 // tiles one after the other (the long and the short one of a causal pair).
-template <int D, int BN, int KSPLIT>
+//
+// ACC: instead of writing O and LSE, merge them into the fp32 accumulator
+// (acc, lse_acc) in the epilogue, as one ring step followed by attn_merge
+// would, without the block's O passing through HBM in bf16.
+template <int D, int BN, int KSPLIT, bool ACC>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf16_kernel(
     FwdParams p) {
   static_assert(BN == 64, "tile of 64 keys");
@@ -381,42 +387,110 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
       m = mm;
     }
 
-    // ---- epilogue: normalise, write O (bf16) and LSE (natural log).  The
-    // wave's 32 O rows pass through LDS (its own 32-row slice of the first
-    // slot of the K buffers, chunks XOR-swizzled by row as the tiles are) so
-    // that every global store writes whole rows.
-    {
-      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-      const uint32_t ln = (uint32_t)lane;
-      const uint32_t ecol = ln & 31u, ehalf = ln >> 5;
-      unsigned char* stage = (wave < 2 ? &k_lds0[0][0] : &k_lds1[0][0]) + (wave & 1) * 32 * RB;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          u32x2_t w;
-          w[0] = pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
-          w[1] = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-          const uint32_t c = (uint32_t)(4 * db + r4) ^ chunk_swz<D>(ecol);
-          *reinterpret_cast<u32x2_t*>(stage + ecol * RB + c * 16 + 8 * ehalf) = w;
+    if constexpr (ACC) {
+      // ---- epilogue: merge (O / l, LSE) into the accumulator rows.  The
+      // weights follow the log1p form of the chunk merge, with the same -inf
+      // guards as attn_merge: a block row with no allowed key leaves the row
+      // alone, an accumulator row at -inf is replaced (never multiplied, so
+      // whatever it holds cannot leak).  The block's rows pass through LDS
+      // in fp32, 16 rows per round in this wave's own 8 KB slice of the
+      // first K buffer slots, so that every accumulator access is a whole
+      // 512-byte row.
+      const float muse = (m == kNegInf) ? 0.f : m;
+      const float lb = ltot > 0.f ? (muse + __log2f(ltot)) * kLn2 : kNegInf;
+      const size_t li = (size_t)head * p.l_q + min(qi, last_row);
+      const float la = p.lse_acc[li];
+      int mode = 0;  // 0 keep, 1 replace, 2 weighted sum
+      float wa = 0.f, wb = 0.f;
+      if (lb != kNegInf) {
+        if (la == kNegInf) {
+          mode = 1;
+          wb = 1.f / ltot;
+          if (half == 0 && qi <= last_row) p.lse_acc[li] = lb;
+        } else {
+          mode = 2;
+          const float mx = fmaxf(la, lb), mn = fminf(la, lb);
+          const float ln = mx + log1pf(expf(mn - mx));
+          wa = expf(la - ln);
+          wb = expf(lb - ln) / ltot;
+          if (half == 0 && qi <= last_row) p.lse_acc[li] = ln;
         }
-      // the wave reads back what its own lanes wrote: LDS operations of one
-      // wave complete in order once counted down
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      constexpr int RPI = 64 / CPR;  // rows per store instruction
-#pragma unroll
-      for (int x = 0; x < 32 / RPI; ++x) {
-        const int r = x * RPI + (int)(ln / CPR);
-        const uint32_t c = (ln % CPR) ^ chunk_swz<D>((uint32_t)r);
-        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stage + r * RB + c * 16);
-        if (iw + r <= last_row)
-          *reinterpret_cast<u32x4_t*>(p.o + ((size_t)b * p.l_q + iw + r) * q_row +
-                                      (size_t)hq * D + 8 * (ln % CPR)) = val;
       }
-      if (half == 0 && qi <= last_row) {
-        const float muse = (m == kNegInf) ? 0.f : m;
-        p.lse[(size_t)head * p.l_q + qi] =
-            ltot > 0.f ? (muse + __log2f(ltot)) * kLn2 : kNegInf;
+      const uint32_t ecol = (uint32_t)lane & 31u, ehalf = (uint32_t)lane >> 5;
+      float* stage = reinterpret_cast<float*>(
+          (wave < 2 ? &k_lds0[0][0] : &k_lds1[0][0]) + (wave & 1) * 32 * RB);
+      constexpr int CH = D / 4;  // 16-byte chunks of an fp32 row
+      static_assert(16 * CH * 16 <= 32 * RB, "16 fp32 rows fit the wave's slice");
+#pragma unroll
+      for (int round = 0; round < 2; ++round) {
+        if ((int)(ecol >> 4) == round) {
+          const uint32_t row = ecol & 15u;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const uint32_t c = (uint32_t)(8 * db + 2 * r4) + ehalf;
+              const f32x4_t x = {oacc[db][4 * r4] * wb, oacc[db][4 * r4 + 1] * wb,
+                                 oacc[db][4 * r4 + 2] * wb, oacc[db][4 * r4 + 3] * wb};
+              *reinterpret_cast<f32x4_t*>(stage + row * D + 4 * (c ^ (2u * row % CH))) = x;
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int it = 0; it < 16 * CH / 64; ++it) {
+          const int k = it * 64 + lane;
+          const int rr = k / CH, c = k % CH;
+          const int src = 16 * round + rr;  // the lane that holds this row
+          const int rmode = __shfl(mode, src);
+          const float rwa = __shfl(wa, src);
+          const int i = iw + src;
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(
+              stage + rr * D + 4 * (c ^ (2 * rr % CH)));
+          if (i <= last_row && rmode != 0) {
+            f32x4_t* dst = reinterpret_cast<f32x4_t*>(
+                p.acc + ((size_t)b * p.l_q + i) * q_row + (size_t)hq * D + 4 * c);
+            *dst = rmode == 1 ? x : *dst * rwa + x;
+          }
+        }
+      }
+    } else {
+      // ---- epilogue: normalise, write O (bf16) and LSE (natural log).  The
+      // wave's 32 O rows pass through LDS (its own 32-row slice of the first
+      // slot of the K buffers, chunks XOR-swizzled by row as the tiles are) so
+      // that every global store writes whole rows.
+      {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        const uint32_t ln = (uint32_t)lane;
+        const uint32_t ecol = ln & 31u, ehalf = ln >> 5;
+        unsigned char* stage = (wave < 2 ? &k_lds0[0][0] : &k_lds1[0][0]) + (wave & 1) * 32 * RB;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            u32x2_t w;
+            w[0] = pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
+            w[1] = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+            const uint32_t c = (uint32_t)(4 * db + r4) ^ chunk_swz<D>(ecol);
+            *reinterpret_cast<u32x2_t*>(stage + ecol * RB + c * 16 + 8 * ehalf) = w;
+          }
+        // the wave reads back what its own lanes wrote: LDS operations of one
+        // wave complete in order once counted down
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+        for (int x = 0; x < 32 / RPI; ++x) {
+          const int r = x * RPI + (int)(ln / CPR);
+          const uint32_t c = (ln % CPR) ^ chunk_swz<D>((uint32_t)r);
+          const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stage + r * RB + c * 16);
+          if (iw + r <= last_row)
+            *reinterpret_cast<u32x4_t*>(p.o + ((size_t)b * p.l_q + iw + r) * q_row +
+                                        (size_t)hq * D + 8 * (ln % CPR)) = val;
+        }
+        if (half == 0 && qi <= last_row) {
+          const float muse = (m == kNegInf) ? 0.f : m;
+          p.lse[(size_t)head * p.l_q + qi] =
+              ltot > 0.f ? (muse + __log2f(ltot)) * kLn2 : kNegInf;
+        }
       }
     }
   };
@@ -615,13 +689,15 @@ FwdSchedule pick_schedule(const FwdParams& p) {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
                            void* out, float* lse, const AttnShape& s,
-                           hipStream_t stream) {
+                           hipStream_t stream, float* acc, float* lse_acc) {
   FwdParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
   p.o = static_cast<uint16_t*>(out);
   p.lse = lse;
+  p.acc = acc;
+  p.lse_acc = lse_acc;
   p.l_q = s.l_q;
   p.l_k = s.l_k;
   p.h = s.h;
@@ -640,16 +716,32 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
   p.pairs = sch == FwdSchedule::kPairs ? 1 : 0;
   p.n_units = p.pairs ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   dim3 grid((unsigned)p.n_units * (unsigned)p.n_heads);
-  if (sch != FwdSchedule::kOneGroup) {
-    if (s.d == 128)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 2>), grid, dim3(2 * kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 2>), grid, dim3(2 * kThreads), 0, stream, p);
+  const bool split = sch != FwdSchedule::kOneGroup;
+  const dim3 block(split ? 2 * kThreads : kThreads);
+  if (acc == nullptr) {
+    if (split) {
+      if (s.d == 128)
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 2, false>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 2, false>), grid, block, 0, stream, p);
+    } else {
+      if (s.d == 128)
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 1, false>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 1, false>), grid, block, 0, stream, p);
+    }
   } else {
-    if (s.d == 128)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 1>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 1>), grid, dim3(kThreads), 0, stream, p);
+    if (split) {
+      if (s.d == 128)
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 2, true>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 2, true>), grid, block, 0, stream, p);
+    } else {
+      if (s.d == 128)
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 1, true>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 1, true>), grid, block, 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

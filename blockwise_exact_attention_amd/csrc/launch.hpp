@@ -14,9 +14,12 @@ struct AttnShape {
   int causal;     // used only for the longest-first tile order
 };
 
+// acc != nullptr: merge the result into the fp32 accumulator (acc, lse_acc)
+// instead of writing out and lse.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
                            void* out, float* lse, const AttnShape& s,
-                           hipStream_t stream);
+                           hipStream_t stream, float* acc = nullptr,
+                           float* lse_acc = nullptr);
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
                           void* out, float* lse, const AttnShape& s,
                           hipStream_t stream);

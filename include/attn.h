@@ -64,7 +64,7 @@ enum attn_status {
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL                        */
   ATTN_ERR_SHAPE = 2,       /* a size is <= 0, h % h_kv != 0, or sizes overflow  */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite
-                               scale, or fp32 backward                           */
+                               scale, or fp32 backward / fused ring step         */
   ATTN_ERR_HIP = 4,         /* the HIP runtime reported a launch failure         */
   ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
   ATTN_ERR_ALIAS = 6,       /* an input buffer overlaps an output buffer         */
@@ -113,6 +113,30 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
                const float* lse_blk, int n, int l, int h, int d, int blk_dtype,
                void* stream);
+
+/*
+ * attn_fwd_acc - one ring step fused: attention of q against this key/value
+ * chunk, merged straight into the ring accumulator (flash_sharding.py
+ * ring_fwd and picotron ring_attention_forward: the fwd call on the chunk
+ * followed by the merge).  The result equals attn_fwd into a block (O, LSE)
+ * followed by attn_merge of that block, except that the block's O is merged
+ * in float32 instead of being rounded to the query dtype first; the same
+ * -inf guards apply (a row with no allowed key in this chunk is left alone;
+ * an accumulator row at -inf is replaced, whatever it held).
+ *
+ *   q       [n,l_q,h,d]     in      bfloat16 (dtype must be ATTN_BF16)
+ *   k,v     [n,l_k,h_kv,d]  in      bfloat16
+ *   out_acc [n,l_q,h,d]     in/out  float32
+ *   lse_acc [n,h,l_q]       in/out  float32, natural log
+ *   d in {64, 128}; any finite scale; masking as for attn_fwd.
+ * out_acc and lse_acc must not overlap each other or q, k, v.  Rows of
+ * different query tiles are merged by different workgroups, so two calls on
+ * the same accumulator must be ordered (one stream, or an event between).
+ */
+int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
+                 float* lse_acc, int n, int l_q, int l_k, int h, int h_kv, int d,
+                 float scale, int causal, int win_l, int win_r,
+                 long long q_offset, long long k_offset, void* stream, int dtype);
 
 /*
  * attn_acc_init - set a ring accumulator to the empty result, O = 0 and

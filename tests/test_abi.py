@@ -36,8 +36,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_merge", "attn_bwd", "attn_acc_init",
-              "attn_acc_cast", "attn_bwd_workspace_bytes",
+    for n in ("attn_fwd", "attn_fwd_acc", "attn_merge", "attn_bwd",
+              "attn_acc_init", "attn_acc_cast", "attn_bwd_workspace_bytes",
               "attn_status_string"):
         assert n in names
 
@@ -65,6 +65,33 @@ def _fwd(**kw):
                                a["d"], a["scale"], a["causal"], a["win_l"],
                                a["win_r"], a["q_offset"], a["k_offset"],
                                a["stream"], a["dtype"])
+
+
+def _fwd_acc(**kw):
+    a = dict(q=A, k=B, v=C, acc=D_, lse=E, n=1, l_q=128, l_k=128, h=2, h_kv=2,
+             d=64, scale=0.125, causal=0, win_l=-1, win_r=-1, q_offset=0,
+             k_offset=0, stream=None, dtype=ATTN_BF16)
+    a.update(kw)
+    return _lib.lib().attn_fwd_acc(a["q"], a["k"], a["v"], a["acc"], a["lse"],
+                                   a["n"], a["l_q"], a["l_k"], a["h"], a["h_kv"],
+                                   a["d"], a["scale"], a["causal"], a["win_l"],
+                                   a["win_r"], a["q_offset"], a["k_offset"],
+                                   a["stream"], a["dtype"])
+
+
+def test_fwd_acc_argument_checks():
+    """The fused ring step rejects what attn_fwd rejects, and fp32 inputs
+    (the accumulator here is 128*2*64*4 = 64 KiB from D_)."""
+    for f in ("q", "k", "v", "acc", "lse"):
+        assert _fwd_acc(**{f: None}) == ATTN_ERR_NULL
+    assert _fwd_acc(h=6, h_kv=4) == ATTN_ERR_SHAPE
+    assert _fwd_acc(d=96) == ATTN_ERR_UNSUPPORTED
+    assert _fwd_acc(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    assert _fwd_acc(acc=D_ + 8) == ATTN_ERR_ALIGN
+    assert _fwd_acc(lse=E + 2) == ATTN_ERR_ALIGN
+    assert _fwd_acc(acc=A + 64) == ATTN_ERR_ALIAS
+    assert _fwd_acc(lse=D_ + 1024) == ATTN_ERR_ALIAS
+    assert _fwd_acc(lse=C + 16) == ATTN_ERR_ALIAS
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "out", "lse"])

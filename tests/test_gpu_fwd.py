@@ -68,15 +68,17 @@ def test_c3_ring_share():
     kc = [dev(c, "bf16") for c in x["k_chunks"]]
     vc = [dev(c, "bf16") for c in x["v_chunks"]]
     share = A.RingShare(tq, w.softmax_scale, True, x["q_offset"])
-    out, lse_acc = share.run(kc, vc, x["k_offsets"])
-    torch.cuda.synchronize()
-    o, lse = host(out), host(lse_acc)
     heads = [(0, 0), (0, 3), (0, 6), (0, 13), (0, 21), (0, 31)]
     q_full_rows = x["q"]
     ro, rl = oracle.attention_fwd(q_full_rows, x["k_full"], x["v_full"],
                                   w.softmax_scale, True, -1, -1,
                                   x["q_offset"], 0, heads=heads)
-    check_o_lse(o, lse, ro, rl, "bf16", "C3 ring share vs full-sequence rows")
+    for fused in (False, True):
+        out, lse_acc = share.run(kc, vc, x["k_offsets"], fused=fused)
+        torch.cuda.synchronize()
+        o, lse = host(out), host(lse_acc)
+        check_o_lse(o, lse, ro, rl, "bf16",
+                    f"C3 ring share (fused={fused}) vs full-sequence rows")
     # the single steps too: step 0 (wholly in the past) and step 7 (diagonal)
     for s in (0, 7):
         ob, lb = run_fwd(x["q"], x["k_chunks"][s], x["v_chunks"][s], "bf16",
@@ -242,10 +244,11 @@ def test_acc_init_and_cast():
     assert torch.all(torch.isneginf(lse_u))
 
 
-def test_small_ring_share_gqa():
+@pytest.mark.parametrize("d,fused", [(128, False), (128, True), (64, True)])
+def test_small_ring_share_gqa(d, fused):
     """A small ring (P = 4 chunks of 96) on every rank, against causal
-    attention over the whole sequence."""
-    P, c, h, h_kv, d = 4, 96, 8, 2, 128
+    attention over the whole sequence; separate and fused ring steps."""
+    P, c, h, h_kv = 4, 96, 8, 2
     q, k, v = rand_inputs(21, 1, P * c, P * c, h, h_kv, d, "bf16")
     ro, rl = oracle.attention_fwd(q, k, v, 0.1, True)
     kc = [dev(k[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
@@ -253,7 +256,60 @@ def test_small_ring_share_gqa():
     for r in range(P):
         tq = dev(q[:, r * c:(r + 1) * c], "bf16")
         out, lse = A.ring_share(tq, kc, vc, [s * c for s in range(P)], r * c,
-                                0.1, True)
+                                0.1, True, fused=fused)
         torch.cuda.synchronize()
         check_o_lse(host(out), host(lse), ro[:, r * c:(r + 1) * c],
                     rl[:, :, r * c:(r + 1) * c], "bf16", f"ring rank {r}")
+
+
+FWD_ACC_CASES = [
+    # n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko
+    (1, 300, 257, 8, 2, 128, True, -1, -1, 0, 100),   # rows 0..99 see no key
+    (2, 190, 333, 4, 4, 64, True, 40, 7, 120, 0),     # window, ragged tiles
+    (1, 1024, 512, 64, 8, 128, False, -1, -1, 0, 0),  # one 4-wave group per tile
+    (1, 128, 1024, 2, 1, 128, True, -1, -1, 896, 0),  # two key groups per tile
+]
+
+
+@pytest.mark.parametrize("case", FWD_ACC_CASES)
+def test_fwd_acc_merges_into_accumulator(case):
+    """attn_fwd_acc on an accumulator holding a previous partial result (some
+    rows empty, with NaN in their O) equals the fp64 merge of that
+    accumulator with the oracle's attention over this chunk."""
+    n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko = case
+    say(f"[fwd_acc] {case}")
+    q, k, v = rand_inputs(31 + l_q + d, n, l_q, l_k, h, h_kv, d, "bf16")
+    rng = np.random.default_rng(l_q + l_k)
+    acc0 = rng.standard_normal((n, l_q, h, d)).astype(np.float32)
+    lse0 = (rng.standard_normal((n, h, l_q)) * 3).astype(np.float32)
+    empty = rng.random((n, h, l_q)) < 0.25
+    lse0[empty] = -np.inf
+    acc_in = acc0.copy()
+    acc_in[np.transpose(empty, (0, 2, 1))] = np.nan
+    heads = [(b, hq) for b in range(n) for hq in sorted({0, h // 2, h - 1})]
+    scale = 1.0 / math.sqrt(d)
+    ob, lb = oracle.attention_fwd(q, k, v, scale, causal, wl, wr, qo, ko,
+                                  heads=heads)
+    sel = ~np.isnan(lb)
+    # rows outside the sampled heads: keep them out of the reference merge
+    lb_m = np.where(sel, lb, -np.inf)
+    ob_m = np.where(np.isnan(ob), 0.0, ob)
+    acc0_clean = np.where(np.isnan(acc_in), 0.0, acc_in)
+    ro, rl = oracle.merge(acc0_clean, lse0, ob_m, lb_m)
+    # a row with no allowed key in this chunk must be left exactly as it was
+    # (NaN content included); it is checked apart from the merged rows
+    keep = sel & np.isneginf(lb)
+    merged = sel & ~keep
+    ro = np.where(np.transpose(merged, (0, 2, 1))[..., None], ro, np.nan)
+    rl = np.where(merged, rl, np.nan)
+    acc = torch.from_numpy(acc_in).cuda()
+    lse_acc = torch.from_numpy(lse0).cuda()
+    A.attn_fwd_acc(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), acc, lse_acc,
+                   scale, causal, wl, wr, qo, ko)
+    torch.cuda.synchronize()
+    go, gl = acc.cpu().numpy(), lse_acc.cpu().numpy()
+    check_o_lse(go.astype(np.float64), gl.astype(np.float64), ro, rl, "bf16",
+                str(case))
+    kr = np.transpose(keep, (0, 2, 1))
+    assert np.array_equal(go[kr], acc_in[kr], equal_nan=True)
+    assert np.array_equal(gl[keep], lse0[keep])
