@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
         const int j0 = kt * BN;
         const bool full = (j0 + BN <= p.l_k) && ((long long)j0 - wb >= p.dlo) &&
                           ((long long)(j0 + BN - 1) - wa <= p.dhi);
-        if (!full) {
+        if (!full && D == 128) {
   #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
   #pragma unroll
@@ -272,6 +272,29 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
               const int rel = j - qi;
               const bool ok = rel >= p.dlo && rel <= p.dhi && j < p.l_k;
               sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+            }
+        } else if (!full) {
+          // Score (kb, r) is key j0 + 4 half + c, c = 32 kb + 8 (r / 4) + r % 4.
+          // This lane's allowed c form one interval lo .. lo + range (from
+          // dlo <= j - qi <= dhi and j < l_k, clamped to the tile; an empty
+          // one gets lo past the tile), so one unsigned compare per score
+          // decides it: half the VALU work of testing the bounds one by one,
+          // which matters where masked tiles are common (the sliding window
+          // at d = 64).  At d = 128 the per-bound form is kept: with it the
+          // compiler schedules the whole step better (measured).
+          const long long base = (long long)qi - j0 - 4 * half;
+          const long long lo64 = max(base + p.dlo, 0LL);
+          const long long hi64 = min(min(base + p.dhi, (long long)p.l_k - 1 - j0 - 4 * half),
+                                     (long long)BN - 1);
+          const bool none = hi64 < lo64;
+          const uint32_t lo = none ? (uint32_t)BN : (uint32_t)lo64;
+          const uint32_t range = none ? 0u : (uint32_t)(hi64 - lo64);
+  #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const uint32_t c = (uint32_t)(32 * kb + 8 * (r >> 2) + (r & 3));
+              sacc[kb][r] = (c - lo) <= range ? sacc[kb][r] : kNegInf;
             }
         }
         float mx = kNegInf;
