@@ -253,6 +253,14 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
     pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, 7168, 1024 * s)
                 for s in range(8))
     fl = fwd_flops(1, 32, 128, pairs)
+    # the ring backward share of the same rank (dO drawn like the inputs)
+    tdo = t(np.random.default_rng(77).standard_normal(x["q"].shape)
+            .astype(np.float32))
+    out, lse = share.run(kc, vc, x["k_offsets"], fused=True)
+    bshare = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, w.softmax_scale,
+                            True, x["q_offset"])
+    bwd_ms = timed(lambda: bshare.run(kc, vc, x["k_offsets"]),
+                   max(5, steps // 4), 2, torch)
     mb = merge_bytes(1, 1024, 32, 128, 2)
     res["ring_share_rank7"] = {
         "fwd_tflops_sum_of_8": round(fl / (sum(fwd_ms) * 1e-3) / 1e12, 2),
@@ -261,7 +269,11 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
         "merge_gbs_warm": round(mb / (merge_ms[0] * 1e-3) / 1e9, 1),
         "end_to_end_ms": round(e2e, 4),
         "end_to_end_fused_ms": round(e2e_fused, 4),
-        "fused_tflops": round(fl / (e2e_fused * 1e-3) / 1e12, 2)}
+        "fused_tflops": round(fl / (e2e_fused * 1e-3) / 1e12, 2),
+        "backward_share_ms": round(bwd_ms, 4),
+        "backward_share_tflops": round(bwd_flops(1, 32, 128, pairs)
+                                       / (bwd_ms * 1e-3) / 1e12, 2)}
+    del bshare, tdo
     del share, kc, vc, tq
 
     # sliding window

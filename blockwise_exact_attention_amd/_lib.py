@@ -36,6 +36,8 @@ SIGNATURES = {
     "attn_acc_cast": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
                       _i, _i, _i, _f, _i, _i, _i, _ll, _ll, _vp, _sz, _vp, _i]),
+    "attn_bwd_acc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                          _i, _i, _i, _f, _i, _i, _i, _ll, _ll, _vp, _sz, _vp, _i]),
     "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
 }

@@ -117,13 +117,17 @@ def attn_fwd_acc(q, k, v, out_acc, lse_acc, scale, causal=False, win_l=-1,
     return out_acc, lse_acc
 
 
-def attn_acc_init(out_acc, lse_acc, stream=None):
-    _dev(out_acc, lse_acc)
+def attn_acc_init(out_acc, lse_acc=None, stream=None):
+    """O = 0 and (unless lse_acc is None) LSE = -inf."""
+    _dev(out_acc, *([] if lse_acc is None else [lse_acc]))
     n, l, h, d = out_acc.shape
-    if tuple(lse_acc.shape) != (n, h, l):
+    if out_acc.dtype != torch.float32:
+        raise ValueError("the accumulator must be float32")
+    if lse_acc is not None and tuple(lse_acc.shape) != (n, h, l):
         raise ValueError("shape mismatch")
-    st = _lib.lib().attn_acc_init(out_acc.data_ptr(), lse_acc.data_ptr(), n, l,
-                                  h, d, _stream(stream))
+    st = _lib.lib().attn_acc_init(out_acc.data_ptr(),
+                                  None if lse_acc is None else lse_acc.data_ptr(),
+                                  n, l, h, d, _stream(stream))
     check("attn_acc_init", st)
     return out_acc, lse_acc
 
@@ -167,6 +171,35 @@ def attn_bwd(dout, q, k, v, out, lse, dq, dk, dv, scale, causal=False,
     return dq, dk, dv
 
 
+def attn_bwd_acc(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, scale,
+                 causal=False, win_l=-1, win_r=-1, q_offset=0, k_offset=0,
+                 workspace=None, stream=None):
+    """One ring backward step: this chunk's gradients added to the float32
+    accumulators dq_acc (shaped like q), dk_acc and dv_acc (shaped like k);
+    out and lse are the query rows' results over the whole sequence."""
+    _dev(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc)
+    n, l_q, h, d = q.shape
+    _, l_k, h_kv, _ = k.shape
+    for a, ref in ((dq_acc, q), (dk_acc, k), (dv_acc, k)):
+        if a.shape != ref.shape or a.dtype != torch.float32:
+            raise ValueError("accumulators must be float32 shaped like q / k")
+    need = bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace)
+    st = _lib.lib().attn_bwd_acc(dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                 v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                 dq_acc.data_ptr(), dk_acc.data_ptr(),
+                                 dv_acc.data_ptr(), n, l_q, l_k, h, h_kv, d,
+                                 float(scale), int(bool(causal)), int(win_l),
+                                 int(win_r), int(q_offset), int(k_offset),
+                                 workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream(stream), _dtype_code(q))
+    check("attn_bwd_acc", st)
+    return dq_acc, dk_acc, dv_acc
+
+
 def attention_backward(dout, q, k, v, out, lse, scale=None, causal=False,
                        window=(-1, -1), q_offset=0, k_offset=0, stream=None):
     if scale is None:
@@ -186,12 +219,13 @@ class RingShare:
     fused=True, the single attn_fwd_acc step, then the final cast - all on
     one stream, nothing synchronised (flash_sharding.py, ring_fwd)."""
 
-    def __init__(self, q, scale, causal, q_offset):
+    def __init__(self, q, scale, causal, q_offset, window=(-1, -1)):
         n, l, h, d = q.shape
         self.q = q
         self.scale = scale
         self.causal = causal
         self.q_offset = q_offset
+        self.window = (int(window[0]), int(window[1]))
         dev = q.device
         self.acc = torch.empty((n, l, h, d), dtype=torch.float32, device=dev)
         self.lse_acc = torch.empty((n, h, l), dtype=torch.float32, device=dev)
@@ -202,12 +236,13 @@ class RingShare:
     def run(self, k_chunks, v_chunks, k_offsets, stream=None, fused=False):
         attn_acc_init(self.acc, self.lse_acc, stream)
         for kc, vc, ko in zip(k_chunks, v_chunks, k_offsets):
+            wl, wr = self.window
             if fused:
                 attn_fwd_acc(self.q, kc, vc, self.acc, self.lse_acc, self.scale,
-                             self.causal, -1, -1, self.q_offset, ko, stream)
+                             self.causal, wl, wr, self.q_offset, ko, stream)
             else:
                 attn_fwd(self.q, kc, vc, self.blk, self.lse_blk, self.scale,
-                         self.causal, -1, -1, self.q_offset, ko, stream)
+                         self.causal, wl, wr, self.q_offset, ko, stream)
                 attn_merge(self.acc, self.lse_acc, self.blk, self.lse_blk,
                            stream)
         attn_acc_cast(self.acc, self.out, stream)
@@ -215,8 +250,55 @@ class RingShare:
 
 
 def ring_share(q, k_chunks, v_chunks, k_offsets, q_offset, scale=None,
-               causal=True, stream=None, fused=False):
+               causal=True, stream=None, fused=False, window=(-1, -1)):
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    return RingShare(q, scale, causal, q_offset).run(k_chunks, v_chunks,
-                                                     k_offsets, stream, fused)
+    return RingShare(q, scale, causal, q_offset, window).run(
+        k_chunks, v_chunks, k_offsets, stream, fused)
+
+
+class RingShareBwd:
+    """One device's share of the ring backward (picotron
+    ring_attention_backward): given its query block q with the forward ring
+    share's final (out, lse) and the incoming gradient dout, `run` adds every
+    key/value chunk's contribution with attn_bwd_acc - dQ accumulating
+    locally in float32, one float32 (dK, dV) accumulator per chunk (in a real
+    ring those travel with the chunk) - and casts dQ to q's dtype at the end.
+    Buffers are allocated once; everything runs on one stream."""
+
+    def __init__(self, q, out, lse, dout, scale, causal, q_offset,
+                 window=(-1, -1)):
+        self.q, self.out, self.lse, self.dout = q, out, lse, dout
+        self.scale = scale
+        self.causal = causal
+        self.q_offset = q_offset
+        self.window = (int(window[0]), int(window[1]))
+        self.dq_acc = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        self.dq = torch.empty_like(q)
+        self.dk_acc = []
+        self.dv_acc = []
+        self.ws = None
+
+    def run(self, k_chunks, v_chunks, k_offsets, stream=None):
+        n, l_q, h, d = self.q.shape
+        if len(self.dk_acc) != len(k_chunks):
+            self.dk_acc = [torch.empty(kc.shape, dtype=torch.float32,
+                                       device=kc.device) for kc in k_chunks]
+            self.dv_acc = [torch.empty(kc.shape, dtype=torch.float32,
+                                       device=kc.device) for kc in k_chunks]
+        if self.ws is None:
+            _, l_k, h_kv, _ = k_chunks[0].shape
+            need = bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d)
+            self.ws = torch.empty(max(need, 1), dtype=torch.uint8,
+                                  device=self.q.device)
+        attn_acc_init(self.dq_acc, None, stream)
+        for kc, vc, ko, dka, dva in zip(k_chunks, v_chunks, k_offsets,
+                                        self.dk_acc, self.dv_acc):
+            attn_acc_init(dka, None, stream)
+            attn_acc_init(dva, None, stream)
+            attn_bwd_acc(self.dout, self.q, kc, vc, self.out, self.lse,
+                         self.dq_acc, dka, dva, self.scale, self.causal,
+                         self.window[0], self.window[1], self.q_offset, ko,
+                         self.ws, stream)
+        attn_acc_cast(self.dq_acc, self.dq, stream)
+        return self.dq, self.dk_acc, self.dv_acc

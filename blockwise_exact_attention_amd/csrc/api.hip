@@ -169,12 +169,12 @@ int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
 
 int attn_acc_init(float* out_acc, float* lse_acc, int n, int l, int h, int d,
                   void* stream) {
-  if (!out_acc || !lse_acc) return ATTN_ERR_NULL;
+  if (!out_acc) return ATTN_ERR_NULL;  // lse_acc may be NULL: O only
   if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;
   if (!aligned(out_acc, 4) || !aligned(lse_acc, 4)) return ATTN_ERR_ALIGN;
   const long long ne = (long long)n * l * h * d;
   const long long nr = (long long)n * l * h;
-  if (overlap(range(out_acc, ne * 4), range(lse_acc, nr * 4)))
+  if (lse_acc && overlap(range(out_acc, ne * 4), range(lse_acc, nr * 4)))
     return ATTN_ERR_ALIAS;
   (void)hipGetLastError();
   return finish(bea::launch_acc_init(out_acc, lse_acc, n, l, h, d,
@@ -203,12 +203,19 @@ size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv,
   return bea::bwd_workspace_bytes(n, l_q, h);
 }
 
-int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
-             const void* out, const float* lse, void* dq, void* dk, void* dv,
-             int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
-             int causal, int win_l, int win_r, long long q_offset,
-             long long k_offset, void* workspace, size_t workspace_bytes,
-             void* stream, int dtype) {
+}  // extern "C"
+
+namespace {
+
+// Shared by attn_bwd and attn_bwd_acc: argument checks (gradient outputs of
+// gb bytes per element), then the launch; acc selects the accumulating
+// kernels (gradients added to fp32 dq, dk, dv).
+int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
+              const void* out, const float* lse, void* dq, void* dk, void* dv,
+              int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
+              int causal, int win_l, int win_r, long long q_offset,
+              long long k_offset, void* workspace, size_t workspace_bytes,
+              void* stream, int dtype, bool acc) {
   if (!dout || !q || !k || !v || !out || !lse || !dq || !dk || !dv)
     return ATTN_ERR_NULL;
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
@@ -221,13 +228,14 @@ int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(workspace, 16))
     return ATTN_ERR_ALIGN;
-  const long long es = dtype == ATTN_BF16 ? 2 : 4;
-  const long long qb = (long long)n * l_q * h * d * es;
-  const long long kb = (long long)n * l_k * h_kv * d * es;
+  const long long es = 2;              // bf16 inputs
+  const long long gb = acc ? 4 : es;   // gradient element bytes
+  const long long qe = (long long)n * l_q * h * d;
+  const long long ke = (long long)n * l_k * h_kv * d;
   const long long lb = (long long)n * h * l_q * 4;
-  const Range ins[] = {range(dout, qb), range(q, qb), range(k, kb),
-                       range(v, kb), range(out, qb), range(lse, lb)};
-  const Range outs[] = {range(dq, qb), range(dk, kb), range(dv, kb),
+  const Range ins[] = {range(dout, qe * es), range(q, qe * es), range(k, ke * es),
+                       range(v, ke * es), range(out, qe * es), range(lse, lb)};
+  const Range outs[] = {range(dq, qe * gb), range(dk, ke * gb), range(dv, ke * gb),
                         range(workspace, (long long)need)};
   for (int a = 0; a < 4; ++a) {
     for (const Range& r : ins)
@@ -238,9 +246,39 @@ int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
   AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
   mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
   (void)hipGetLastError();
-  return finish(bea::launch_bwd(dout, q, k, v, out, lse, dq, dk, dv, s,
-                                workspace, dtype == ATTN_BF16,
-                                static_cast<hipStream_t>(stream)));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (acc)
+    return finish(bea::launch_bwd(dout, q, k, v, out, lse, nullptr, nullptr, nullptr,
+                                  s, workspace, true, hs, static_cast<float*>(dq),
+                                  static_cast<float*>(dk), static_cast<float*>(dv)));
+  return finish(bea::launch_bwd(dout, q, k, v, out, lse, dq, dk, dv, s, workspace,
+                                true, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
+             const void* out, const float* lse, void* dq, void* dk, void* dv,
+             int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
+             int causal, int win_l, int win_r, long long q_offset,
+             long long k_offset, void* workspace, size_t workspace_bytes,
+             void* stream, int dtype) {
+  return bwd_entry(dout, q, k, v, out, lse, dq, dk, dv, n, l_q, l_k, h, h_kv, d,
+                   scale, causal, win_l, win_r, q_offset, k_offset, workspace,
+                   workspace_bytes, stream, dtype, false);
+}
+
+int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
+                 const void* out, const float* lse, float* dq_acc, float* dk_acc,
+                 float* dv_acc, int n, int l_q, int l_k, int h, int h_kv, int d,
+                 float scale, int causal, int win_l, int win_r, long long q_offset,
+                 long long k_offset, void* workspace, size_t workspace_bytes,
+                 void* stream, int dtype) {
+  return bwd_entry(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, n, l_q, l_k, h,
+                   h_kv, d, scale, causal, win_l, win_r, q_offset, k_offset,
+                   workspace, workspace_bytes, stream, dtype, true);
 }
 
 const char* attn_status_string(int status) {

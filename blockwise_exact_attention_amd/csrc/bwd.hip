@@ -43,6 +43,9 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  float* dq_acc;  // ACC kernels: fp32 accumulators the gradients are added to
+  float* dk_acc;
+  float* dv_acc;
   float* dd;    // D [n, h, l_q]
   float* lse2;  // LSE * log2(e) [n, h, l_q]; +inf for empty rows
   int n, l_q, l_k, h, h_kv, grp;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
 constexpr int kKeysPerWave = 32;
 constexpr int kKeysPerWG = 4 * kKeysPerWave;
 
-template <int D>
+template <int D, bool ACC>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int n_ktiles,
                                                                int reverse) {
   constexpr int BQ = 64;         // query rows per tile
@@ -280,6 +283,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
     if (u + 1 < n_steps) step(u + 1, q_lds1, o_lds1, l_lds1, q_lds0, o_lds0, l_lds0);
   }
 
+  if constexpr (ACC) {
+    // ---- epilogue (ACC): dk_acc += scale dK^T, dv_acc += dV^T in fp32; the
+    // lane owns key kj and dims 32 db + 8 r4 + 4 half + 0..3 (16 bytes)
+    if (kj <= last_key) {
+      const size_t off = ((size_t)b * p.l_k + kj) * kv_row + (size_t)g * D + 4 * half;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4_t* k4 = reinterpret_cast<f32x4_t*>(p.dk_acc + off + 32 * db + 8 * r4);
+          f32x4_t* v4 = reinterpret_cast<f32x4_t*>(p.dv_acc + off + 32 * db + 8 * r4);
+          const f32x4_t kx = {dkt[db][4 * r4], dkt[db][4 * r4 + 1], dkt[db][4 * r4 + 2],
+                              dkt[db][4 * r4 + 3]};
+          const f32x4_t vx = {dvt[db][4 * r4], dvt[db][4 * r4 + 1], dvt[db][4 * r4 + 2],
+                              dvt[db][4 * r4 + 3]};
+          *k4 = *k4 + kx * p.scale;
+          *v4 = *v4 + vx;
+        }
+    }
+    return;
+  }
   // ---- epilogue: dK = scale dK^T, dV = dV^T as bf16, 32 key rows per wave
   // staged through LDS (dK rows in the Q buffers, dV rows in the dO buffers,
   // swizzled like the tiles) so that every store writes whole rows
@@ -330,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
 // K^T read transposed out of the row-major K tile reads dS^T straight from
 // registers as its B operand.
 
-template <int D>
+template <int D, bool ACC>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_qtiles,
                                                              int reverse) {
   constexpr int BN = 64;
@@ -481,6 +505,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
     if (kt + 1 < kt_end) step(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
+  if constexpr (ACC) {
+    // ---- epilogue (ACC): dq_acc += scale dQ^T in fp32; the lane owns query
+    // row qi and dims 32 db + 8 r4 + 4 half + 0..3 (16 bytes)
+    if (qi <= last_row) {
+      const size_t off = ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D + 4 * half;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4_t* q4 = reinterpret_cast<f32x4_t*>(p.dq_acc + off + 32 * db + 8 * r4);
+          const f32x4_t x = {dqt[db][4 * r4], dqt[db][4 * r4 + 1], dqt[db][4 * r4 + 2],
+                             dqt[db][4 * r4 + 3]};
+          *q4 = *q4 + x * p.scale;
+        }
+    }
+    return;
+  }
   // ---- epilogue: dQ = scale dQ^T as bf16, the wave's 32 rows staged
   // through LDS (swizzled like the tiles) so that every store writes whole
   // rows
@@ -513,18 +554,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
   }
 }
 
-template <int D>
+template <int D, bool ACC>
 hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream) {
   const long long rows = (long long)p.n * p.l_q * p.h;
   const long long pre_blocks = (rows * (D / 8) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(kThreads),
                      0, stream, p);
   const int n_ktiles = (p.l_k + kKeysPerWG - 1) / kKeysPerWG;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, ACC>),
                      dim3((unsigned)(n_ktiles * p.n * p.h_kv)), dim3(kThreads), 0,
                      stream, p, n_ktiles, causal ? 1 : 0);
   const int n_qtiles = (p.l_q + 127) / 128;
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(n_qtiles * p.n * p.h)),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, ACC>), dim3((unsigned)(n_qtiles * p.n * p.h)),
                      dim3(kThreads), 0, stream, p, n_qtiles, causal ? 1 : 0);
   return hipGetLastError();
 }
@@ -539,7 +580,8 @@ size_t bwd_workspace_bytes(int n, int l_q, int h) {
 hipError_t launch_bwd(const void* dout, const void* q, const void* k,
                       const void* v, const void* out, const float* lse,
                       void* dq, void* dk, void* dv, const AttnShape& s,
-                      void* workspace, bool bf16, hipStream_t stream) {
+                      void* workspace, bool bf16, hipStream_t stream,
+                      float* dq_acc, float* dk_acc, float* dv_acc) {
   if (!bf16) return hipErrorNotSupported;
   BwdParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -551,6 +593,9 @@ hipError_t launch_bwd(const void* dout, const void* q, const void* k,
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
+  p.dq_acc = dq_acc;
+  p.dk_acc = dk_acc;
+  p.dv_acc = dv_acc;
   const size_t rows = (size_t)s.n * s.l_q * s.h;
   p.dd = static_cast<float*>(workspace);
   p.lse2 = static_cast<float*>(workspace) + rows;
@@ -564,8 +609,11 @@ hipError_t launch_bwd(const void* dout, const void* q, const void* k,
   p.scale = s.scale;
   p.dlo = s.dlo;
   p.dhi = s.dhi;
-  return s.d == 128 ? launch_bwd_d<128>(p, s.causal, stream)
-                    : launch_bwd_d<64>(p, s.causal, stream);
+  if (dq_acc != nullptr)
+    return s.d == 128 ? launch_bwd_d<128, true>(p, s.causal, stream)
+                      : launch_bwd_d<64, true>(p, s.causal, stream);
+  return s.d == 128 ? launch_bwd_d<128, false>(p, s.causal, stream)
+                    : launch_bwd_d<64, false>(p, s.causal, stream);
 }
 
 }  // namespace bea

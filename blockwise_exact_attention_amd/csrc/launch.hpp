@@ -33,9 +33,13 @@ hipError_t launch_acc_cast(const float* out_acc, void* out, int n, int l,
                            int h, int d, bool bf16, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int n, int l_q, int h);
+// dq_acc != nullptr: add the gradients to the fp32 accumulators (dq_acc,
+// dk_acc, dv_acc) instead of writing dq, dk, dv.
 hipError_t launch_bwd(const void* dout, const void* q, const void* k,
                       const void* v, const void* out, const float* lse,
                       void* dq, void* dk, void* dv, const AttnShape& s,
-                      void* workspace, bool bf16, hipStream_t stream);
+                      void* workspace, bool bf16, hipStream_t stream,
+                      float* dq_acc = nullptr, float* dk_acc = nullptr,
+                      float* dv_acc = nullptr);
 
 }  // namespace bea

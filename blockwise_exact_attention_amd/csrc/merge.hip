@@ -264,7 +264,7 @@ hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
 hipError_t launch_acc_init(float* out_acc, float* lse_acc, int n, int l, int h,
                            int d, hipStream_t stream) {
   const long long n_acc = (long long)n * l * h * d;
-  const long long n_lse = (long long)n * l * h;
+  const long long n_lse = lse_acc != nullptr ? (long long)n * l * h : 0;
   const long long n4 = (reinterpret_cast<uintptr_t>(out_acc) % 16 == 0) ? n_acc / 4 : 0;
   hipLaunchKernelGGL(acc_init_kernel, dim3(grid_for(n_acc / 4 + 1, 256)), dim3(256),
                      0, stream, out_acc, lse_acc, n_acc, n4, n_lse);

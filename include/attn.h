@@ -141,7 +141,8 @@ int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
 /*
  * attn_acc_init - set a ring accumulator to the empty result, O = 0 and
  * LSE = -inf (flash_sharding.py ring_fwd, its initial o and lse).
- *   out_acc [n,l,h,d] float32 out; lse_acc [n,h,l] float32 out.
+ *   out_acc [n,l,h,d] float32 out; lse_acc [n,h,l] float32 out, or NULL to
+ *   zero out_acc only (the gradient accumulators of attn_bwd_acc).
  */
 int attn_acc_init(float* out_acc, float* lse_acc, int n, int l, int h, int d,
                   void* stream);
@@ -177,6 +178,32 @@ int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
              float scale, int causal, int win_l, int win_r,
              long long q_offset, long long k_offset,
              void* workspace, size_t workspace_bytes, void* stream, int dtype);
+
+/*
+ * attn_bwd_acc - one step of the ring backward as one device sees it
+ * (picotron ring_attention_backward; flash_sharding.py ring_bwd): the
+ * gradient contributions of this key/value chunk, added to float32
+ * accumulators instead of written:
+ *   dq_acc += scale dS K,  dk_acc += scale dS^T Q,  dv_acc += P^T dout,
+ * with P = exp(S - lse), D = rowsum(dout * out), dS = P (dP - D), as in
+ * attn_bwd.  For a ring step, out and lse are the query rows' results over
+ * the whole sequence (the forward ring share's final O and LSE), so that P is
+ * the global softmax restricted to this chunk; summing the steps then gives
+ * the full gradients.  dk_acc / dv_acc of a chunk collect the contributions
+ * of every query block that reads it (in a real ring they travel with the
+ * chunk).
+ *   dout, q, out [n,l_q,h,d] bf16; k, v [n,l_k,h_kv,d] bf16; lse [n,h,l_q]
+ *   dq_acc [n,l_q,h,d] float32 in/out; dk_acc, dv_acc [n,l_k,h_kv,d]
+ *   float32 in/out; workspace as for attn_bwd; dtype must be ATTN_BF16.
+ * The accumulators must not overlap the inputs, the workspace or each other;
+ * calls that add to the same accumulator must be ordered on one stream.
+ */
+int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
+                 const void* out, const float* lse, float* dq_acc, float* dk_acc,
+                 float* dv_acc, int n, int l_q, int l_k, int h, int h_kv, int d,
+                 float scale, int causal, int win_l, int win_r,
+                 long long q_offset, long long k_offset,
+                 void* workspace, size_t workspace_bytes, void* stream, int dtype);
 
 /* Bytes of workspace attn_bwd needs for these sizes (0 on invalid sizes). */
 size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);

@@ -37,8 +37,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_acc", "attn_merge", "attn_bwd",
-              "attn_acc_init", "attn_acc_cast", "attn_bwd_workspace_bytes",
-              "attn_status_string"):
+              "attn_bwd_acc", "attn_acc_init", "attn_acc_cast",
+              "attn_bwd_workspace_bytes", "attn_status_string"):
         assert n in names
 
 
@@ -191,3 +191,30 @@ def test_allowed_pairs_matches_oracle_mask():
     assert allowed_pairs(4096, 4096, True, 256, 0) == 1019776
     assert allowed_pairs(1024, 1024, True, -1, -1, 7168, 7168) == 524800
     assert allowed_pairs(16384, 16384, True) == 134225920
+
+
+def test_bwd_acc_checks():
+    """The accumulating backward checks its arguments like attn_bwd, with
+    float32 gradient accumulators: dk_acc starting 48 KiB into dq_acc
+    (128*2*64*4 = 64 KiB) is an alias.  Every call here fails a check, so
+    nothing is launched."""
+    L = _lib.lib()
+    need = L.attn_bwd_workspace_bytes(1, 128, 128, 2, 2, 64)
+    ptrs = [A, A + (1 << 28), B, B + (1 << 28), C, C + (1 << 28), D_,
+            D_ + (1 << 28), E]
+
+    def call(ptrs=ptrs, ws=F, wsb=need, dtype=ATTN_BF16):
+        return L.attn_bwd_acc(*ptrs, 1, 128, 128, 2, 2, 64, 0.125, 1, -1, -1,
+                              0, 0, ws, wsb, None, dtype)
+    for i in range(9):
+        bad = list(ptrs)
+        bad[i] = None
+        assert call(ptrs=bad) == ATTN_ERR_NULL
+    assert call(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    assert call(wsb=need - 1) == ATTN_ERR_WORKSPACE
+    mis = list(ptrs)
+    mis[6] = D_ + 4
+    assert call(ptrs=mis) == ATTN_ERR_ALIGN
+    near = list(ptrs)
+    near[7] = D_ + 48 * 1024    # dk_acc inside dq_acc's 64 KiB
+    assert call(ptrs=near) == ATTN_ERR_ALIAS

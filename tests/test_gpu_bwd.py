@@ -122,3 +122,74 @@ def test_fp32_backward_is_rejected():
     lse = torch.zeros((1, 2, 64), device="cuda")
     with pytest.raises(A.AttnError if hasattr(A, "AttnError") else Exception):
         A.attention_backward(q, q, q, q, q, lse)
+
+
+@pytest.mark.parametrize("d,h_kv,window,fused", [
+    (128, 2, (-1, -1), True),
+    (64, 1, (-1, -1), False),
+    (128, 2, (100, 0), True),
+])
+def test_ring_share_backward(d, h_kv, window, fused):
+    """The ring backward as each of P = 4 ranks sees it (chunks of 96, causal):
+    forward ring share for the rank's queries, then one attn_bwd_acc per
+    chunk with the share's final (O, LSE).  dQ must equal the rank's rows of
+    the full-sequence gradient, and each chunk's (dK, dV) accumulator the
+    contribution of the rank's queries to that chunk's keys - the oracle's
+    backward of the rank's query block against the whole sequence."""
+    P, c, h = 4, 96, 8
+    L = P * c
+    q, k, v, do = draw_normal(41 + d + h_kv, [(1, L, h, d), (1, L, h_kv, d),
+                                              (1, L, h_kv, d), (1, L, h, d)])
+    q, k, v, do = (round_to_bf16(x) for x in (q, k, v, do))
+    scale = 1.0 / math.sqrt(d)
+    kc = [dev(k[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
+    vc = [dev(v[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
+    offs = [s * c for s in range(P)]
+    for r in range(P):
+        say(f"[ring bwd] d={d} h_kv={h_kv} window={window} rank {r}")
+        qr, dor = q[:, r * c:(r + 1) * c], do[:, r * c:(r + 1) * c]
+        tq, tdo = dev(qr, "bf16"), dev(dor, "bf16")
+        out, lse = A.ring_share(tq, kc, vc, offs, r * c, scale, True,
+                                fused=fused, window=window)
+        share = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, scale, True,
+                               r * c, window)
+        dq, dk_acc, dv_acc = share.run(kc, vc, offs)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.attention_bwd(qr, k, v, dor, scale, True, window[0],
+                                          window[1], r * c, 0)
+        check_grad(host(dq), rq, f"rank {r} dq")
+        for s in range(P):
+            check_grad(host(dk_acc[s]), rk[:, s * c:(s + 1) * c],
+                       f"rank {r} chunk {s} dk")
+            check_grad(host(dv_acc[s]), rv[:, s * c:(s + 1) * c],
+                       f"rank {r} chunk {s} dv")
+
+
+def test_c3_ring_share_backward():
+    """The ring backward share of rank 7 at the ring workload's full size
+    (1024 query rows, 8 chunks of 1024 keys, GQA 32/8), on two key/value
+    groups: dQ and the per-chunk (dK, dV) accumulators against the oracle's
+    backward of rank 7's queries over the whole 8192-token sequence."""
+    w = WORKLOADS["C3"]
+    say(f"[C3 ring bwd] {w}")
+    x = make_inputs(w)
+    rng = np.random.default_rng(77)
+    do = round_to_bf16(rng.standard_normal(x["q"].shape).astype(np.float32))
+    tq, tdo = dev(x["q"], "bf16"), dev(do, "bf16")
+    kc = [dev(cc, "bf16") for cc in x["k_chunks"]]
+    vc = [dev(cc, "bf16") for cc in x["v_chunks"]]
+    out, lse = A.ring_share(tq, kc, vc, x["k_offsets"], x["q_offset"],
+                            w.softmax_scale, True, fused=True)
+    share = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, w.softmax_scale,
+                           True, x["q_offset"])
+    dq, dk_acc, dv_acc = share.run(kc, vc, x["k_offsets"])
+    torch.cuda.synchronize()
+    groups = [(0, 0), (0, 7)]
+    rq, rk, rv = oracle.attention_bwd(x["q"], x["k_full"], x["v_full"], do,
+                                      w.softmax_scale, True, -1, -1,
+                                      x["q_offset"], 0, kv_heads=groups)
+    check_grad(host(dq), rq, "C3 rank 7 dq")
+    c = w.l_k
+    for s in (0, 3, 7):
+        check_grad(host(dk_acc[s]), rk[:, s * c:(s + 1) * c], f"C3 chunk {s} dk")
+        check_grad(host(dv_acc[s]), rv[:, s * c:(s + 1) * c], f"C3 chunk {s} dv")

@@ -262,6 +262,31 @@ def test_small_ring_share_gqa(d, fused):
                     rl[:, :, r * c:(r + 1) * c], "bf16", f"ring rank {r}")
 
 
+
+@pytest.mark.parametrize("d,h_kv,causal,window,fused", [
+    (128, 1, True, (100, 0), False),
+    (64, 1, True, (100, 0), True),
+    (128, 2, False, (50, 30), True),
+])
+def test_ring_share_sliding_window(d, h_kv, causal, window, fused):
+    """Sliding-window attention in ring mode (P = 4 chunks of 96, multi-query
+    and grouped heads): each rank's share equals its rows of windowed
+    attention over the whole sequence; chunks wholly outside a rank's window
+    are empty steps that must leave the accumulator alone."""
+    P, c, h = 4, 96, 8
+    q, k, v = rand_inputs(23 + d + h_kv, 1, P * c, P * c, h, h_kv, d, "bf16")
+    scale = 1.0 / math.sqrt(d)
+    ro, rl = oracle.attention_fwd(q, k, v, scale, causal, window[0], window[1])
+    kc = [dev(k[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
+    vc = [dev(v[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
+    for r in range(P):
+        tq = dev(q[:, r * c:(r + 1) * c], "bf16")
+        out, lse = A.ring_share(tq, kc, vc, [s * c for s in range(P)], r * c,
+                                scale, causal, fused=fused, window=window)
+        torch.cuda.synchronize()
+        check_o_lse(host(out), host(lse), ro[:, r * c:(r + 1) * c],
+                    rl[:, :, r * c:(r + 1) * c], "bf16", f"window ring rank {r}")
+
 FWD_ACC_CASES = [
     # n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko
     (1, 300, 257, 8, 2, 128, True, -1, -1, 0, 100),   # rows 0..99 see no key
