@@ -200,7 +200,7 @@ size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv,
                                 int d) {
   if (!sizes_ok(n, l_q, h, d) || !sizes_ok(n, l_k, h_kv, d)) return 0;
   if (h % h_kv != 0) return 0;
-  return bea::bwd_workspace_bytes(n, l_q, h);
+  return bea::bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d);
 }
 
 }  // extern "C"
@@ -221,7 +221,7 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  const size_t need = bea::bwd_workspace_bytes(n, l_q, h);
+  const size_t need = bea::bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) ||
       !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||

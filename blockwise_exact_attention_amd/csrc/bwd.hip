@@ -24,6 +24,8 @@
 //    straight from registers; K^T is read transposed out of the K tile.
 // Tiles use the layout of the forward kernel (swizzled rows, direct loads,
 // two buffers one tile ahead).
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
@@ -46,6 +48,11 @@ struct BwdParams {
   float* dq_acc;  // ACC kernels: fp32 accumulators the gradients are added to
   float* dk_acc;
   float* dv_acc;
+  float* part;      // split dK/dV: per-slice fp32 partials (dK at part, dV
+  size_t part_half; //   part_half floats later), each [n, l_k, h_kv, d]
+  int* counters;    // split dK/dV: arrivals per (key tile, head), zeroed by bwd_pre
+  int n_counters;
+  int split;        // slices of the query steps per key tile (1: no split)
   float* dd;    // D [n, h, l_q]
   float* lse2;  // LSE * log2(e) [n, h, l_q]; +inf for empty rows
   int n, l_q, l_k, h, h_kv, grp;
@@ -62,6 +69,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
   const long long rows = (long long)p.n * p.l_q * p.h;
   const long long row = ((long long)blockIdx.x * kThreads + threadIdx.x) / TPR;
   const int part = threadIdx.x % TPR;
+  for (long long c = (long long)blockIdx.x * kThreads + threadIdx.x; c < p.n_counters;
+       c += (long long)gridDim.x * kThreads)
+    p.counters[c] = 0;
   float acc = 0.f;
   const bool ok = row < rows;
   const long long rr = ok ? row : rows - 1;
@@ -128,11 +138,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // blockIdx.x -> (key tile, b * h_kv + g); under causal masking the first
-  // key tiles are read by the most query rows: they go first
+  // blockIdx.x -> (slice, key tile, b * h_kv + g); under causal masking the
+  // first key tiles are read by the most query rows: they go first
   const int heads = p.n * p.h_kv;
-  const int rank = blockIdx.x / heads;
-  const int kvh = blockIdx.x - rank * heads;
+  const int tiles_heads = n_ktiles * heads;
+  const int slice = blockIdx.x / tiles_heads;
+  const int wid = blockIdx.x - slice * tiles_heads;
+  const int rank = wid / heads;
+  const int kvh = wid - rank * heads;
   const int kt = reverse ? rank : n_ktiles - 1 - rank;
   const int b = kvh / p.h_kv;
   const int g = kvh - b * p.h_kv;
@@ -179,6 +192,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
   const int t_begin = qlo <= qhi ? (int)(qlo / BQ) : 0;
   const int nt = qlo <= qhi ? (int)(qhi / BQ) + 1 - t_begin : 0;
   const int n_steps = nt * p.grp;
+  // this workgroup's slice of the steps
+  const int u_lo = (int)((long long)slice * n_steps / p.split);
+  const int u_end = (int)((long long)(slice + 1) * n_steps / p.split);
   auto load = [&](int u, unsigned char* qd, unsigned char* od, float* ld) {
     const int hq = g * p.grp + u / nt;
     const int i0 = (t_begin + u % nt) * BQ;
@@ -196,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
   };
   auto step = [&](int u, const unsigned char* ql, const unsigned char* ol, const float* ll,
                   unsigned char* qn, unsigned char* on, float* ln) {
-    if (u + 1 < n_steps) load(u + 1, qn, on, ln);
+    if (u + 1 < u_end) load(u + 1, qn, on, ln);
     const int i0 = (t_begin + u % nt) * BQ;
     const int i_last = min(i0 + BQ - 1, p.l_q - 1);
     const bool live = wave_live && (long long)kw_last - i0 >= p.dlo &&
@@ -272,15 +288,68 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads landed
     __syncthreads();
   };
-  if (n_steps > 0) {
-    load(0, q_lds0, o_lds0, l_lds0);
+  if (u_lo < u_end) {
+    load(u_lo, q_lds0, o_lds0, l_lds0);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
   // unrolled by two so that every buffer reference is a fixed LDS object
-  for (int u = 0; u < n_steps; u += 2) {
+  for (int u = u_lo; u < u_end; u += 2) {
     step(u, q_lds0, o_lds0, l_lds0, q_lds1, o_lds1, l_lds1);
-    if (u + 1 < n_steps) step(u + 1, q_lds1, o_lds1, l_lds1, q_lds0, o_lds0, l_lds0);
+    if (u + 1 < u_end) step(u + 1, q_lds1, o_lds1, l_lds1, q_lds0, o_lds0, l_lds0);
+  }
+
+  if (p.split > 1) {
+    // ---- split: every slice stores its partial dK^T, dV^T (fp32, the
+    // lane's key and dims 32 db + 8 r4 + 4 half + 0..3); the last slice of
+    // this key tile to arrive adds all of them up, slice 0 first, so the
+    // result does not depend on the arrival order, and runs the epilogue.
+    __shared__ int s_last;
+    const size_t poff = ((size_t)b * p.l_k + min(kj, last_key)) * kv_row +
+                        (size_t)g * D + 4 * half;
+    float* pk = p.part + (size_t)slice * 2 * p.part_half;
+    if (kj <= last_key) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          *reinterpret_cast<f32x4_t*>(pk + poff + 32 * db + 8 * r4) =
+              f32x4_t{dkt[db][4 * r4], dkt[db][4 * r4 + 1], dkt[db][4 * r4 + 2],
+                      dkt[db][4 * r4 + 3]};
+          *reinterpret_cast<f32x4_t*>(pk + p.part_half + poff + 32 * db + 8 * r4) =
+              f32x4_t{dvt[db][4 * r4], dvt[db][4 * r4 + 1], dvt[db][4 * r4 + 2],
+                      dvt[db][4 * r4 + 3]};
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&p.counters[wid], 1) == p.split - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkt[db][r] = 0.f;
+        dvt[db][r] = 0.f;
+      }
+    for (int sl = 0; sl < p.split; ++sl) {
+      const float* qk = p.part + (size_t)sl * 2 * p.part_half;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t xk = *reinterpret_cast<const f32x4_t*>(qk + poff + 32 * db + 8 * r4);
+          const f32x4_t xv =
+              *reinterpret_cast<const f32x4_t*>(qk + p.part_half + poff + 32 * db + 8 * r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dkt[db][4 * r4 + e] += xk[e];
+            dvt[db][4 * r4 + e] += xv[e];
+          }
+        }
+    }
   }
 
   if constexpr (ACC) {
@@ -554,6 +623,41 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
   }
 }
 
+// dK/dV workgroups per (key tile, key/value head) pair: when the key tiles
+// alone give fewer than two workgroups per CU, the query steps of each key
+// tile are split over up to four workgroups whose partial sums are added
+// deterministically by the last one to finish.
+constexpr int kDkdvTargetWGs = 512;
+
+int dkdv_split(int n, int l_k, int h_kv) {
+  const long long w = (long long)((l_k + kKeysPerWG - 1) / kKeysPerWG) * n * h_kv;
+  if (w >= kDkdvTargetWGs) return 1;
+  return (int)std::min<long long>(4, (kDkdvTargetWGs + w - 1) / w);
+}
+
+// Workspace layout: D and LSE2 per query row, then (split > 1) the per-slice
+// dK, dV partials and the arrival counters, each part 256-byte aligned.
+struct BwdWorkspace {
+  size_t dd, lse2, part, counters, total;
+  size_t part_half;  // floats in one partial dK (or dV)
+  int split, n_counters;
+};
+
+BwdWorkspace bwd_layout(int n, int l_q, int l_k, int h, int h_kv, int d) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  BwdWorkspace w;
+  const size_t rows = (size_t)n * l_q * h;
+  w.split = dkdv_split(n, l_k, h_kv);
+  w.n_counters = w.split > 1 ? ((l_k + kKeysPerWG - 1) / kKeysPerWG) * n * h_kv : 0;
+  w.part_half = w.split > 1 ? (size_t)n * l_k * h_kv * d : 0;
+  w.dd = 0;
+  w.lse2 = up(rows * 4);
+  w.part = w.lse2 + up(rows * 4);
+  w.counters = w.part + up((size_t)w.split * 2 * w.part_half * 4 * (w.split > 1));
+  w.total = w.counters + up((size_t)w.n_counters * 4);
+  return w;
+}
+
 template <int D, bool ACC>
 hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream) {
   const long long rows = (long long)p.n * p.l_q * p.h;
@@ -562,8 +666,8 @@ hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream) {
                      0, stream, p);
   const int n_ktiles = (p.l_k + kKeysPerWG - 1) / kKeysPerWG;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, ACC>),
-                     dim3((unsigned)(n_ktiles * p.n * p.h_kv)), dim3(kThreads), 0,
-                     stream, p, n_ktiles, causal ? 1 : 0);
+                     dim3((unsigned)(p.split * n_ktiles * p.n * p.h_kv)), dim3(kThreads),
+                     0, stream, p, n_ktiles, causal ? 1 : 0);
   const int n_qtiles = (p.l_q + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_kernel<D, ACC>), dim3((unsigned)(n_qtiles * p.n * p.h)),
                      dim3(kThreads), 0, stream, p, n_qtiles, causal ? 1 : 0);
@@ -572,9 +676,8 @@ hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int n, int l_q, int h) {
-  // D and LSE*log2(e), one float each per query row
-  return (size_t)2 * n * l_q * h * sizeof(float);
+size_t bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d) {
+  return bwd_layout(n, l_q, l_k, h, h_kv, d).total;
 }
 
 hipError_t launch_bwd(const void* dout, const void* q, const void* k,
@@ -596,9 +699,15 @@ hipError_t launch_bwd(const void* dout, const void* q, const void* k,
   p.dq_acc = dq_acc;
   p.dk_acc = dk_acc;
   p.dv_acc = dv_acc;
-  const size_t rows = (size_t)s.n * s.l_q * s.h;
-  p.dd = static_cast<float*>(workspace);
-  p.lse2 = static_cast<float*>(workspace) + rows;
+  const BwdWorkspace w = bwd_layout(s.n, s.l_q, s.l_k, s.h, s.h_kv, s.d);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  p.dd = reinterpret_cast<float*>(ws + w.dd);
+  p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
+  p.part = reinterpret_cast<float*>(ws + w.part);
+  p.part_half = w.part_half;
+  p.counters = reinterpret_cast<int*>(ws + w.counters);
+  p.n_counters = w.n_counters;
+  p.split = w.split;
   p.n = s.n;
   p.l_q = s.l_q;
   p.l_k = s.l_k;

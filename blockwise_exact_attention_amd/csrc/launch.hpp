@@ -32,7 +32,7 @@ hipError_t launch_acc_init(float* out_acc, float* lse_acc, int n, int l, int h,
 hipError_t launch_acc_cast(const float* out_acc, void* out, int n, int l,
                            int h, int d, bool bf16, hipStream_t stream);
 
-size_t bwd_workspace_bytes(int n, int l_q, int h);
+size_t bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);
 // dq_acc != nullptr: add the gradients to the fp32 accumulators (dq_acc,
 // dk_acc, dv_acc) instead of writing dq, dk, dv.
 hipError_t launch_bwd(const void* dout, const void* q, const void* k,
