@@ -50,8 +50,6 @@ struct BwdParams {
   float* dv_acc;
   float* part;      // split dK/dV: per-slice fp32 partials (dK at part, dV
   size_t part_half; //   part_half floats later), each [n, l_k, h_kv, d]
-  int* counters;    // split dK/dV: arrivals per (key tile, head), zeroed by bwd_pre
-  int n_counters;
   int split;        // slices of the query steps per key tile (1: no split)
   float* dd;    // D [n, h, l_q]
   float* lse2;  // LSE * log2(e) [n, h, l_q]; +inf for empty rows
@@ -69,9 +67,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
   const long long rows = (long long)p.n * p.l_q * p.h;
   const long long row = ((long long)blockIdx.x * kThreads + threadIdx.x) / TPR;
   const int part = threadIdx.x % TPR;
-  for (long long c = (long long)blockIdx.x * kThreads + threadIdx.x; c < p.n_counters;
-       c += (long long)gridDim.x * kThreads)
-    p.counters[c] = 0;
   float acc = 0.f;
   const bool ok = row < rows;
   const long long rr = ok ? row : rows - 1;
@@ -301,12 +296,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
 
   if (p.split > 1) {
     // ---- split: every slice stores its partial dK^T, dV^T (fp32, the
-    // lane's key and dims 32 db + 8 r4 + 4 half + 0..3); the last slice of
-    // this key tile to arrive adds all of them up, slice 0 first, so the
-    // result does not depend on the arrival order, and runs the epilogue.
-    __shared__ int s_last;
-    const size_t poff = ((size_t)b * p.l_k + min(kj, last_key)) * kv_row +
-                        (size_t)g * D + 4 * half;
+    // lane's key and dims 32 db + 8 r4 + 4 half + 0..3); bwd_dkdv_reduce
+    // adds them up (slice 0 first) and writes dK, dV
+    const size_t poff = ((size_t)b * p.l_k + kj) * kv_row + (size_t)g * D + 4 * half;
     float* pk = p.part + (size_t)slice * 2 * p.part_half;
     if (kj <= last_key) {
 #pragma unroll
@@ -321,35 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
                       dvt[db][4 * r4 + 3]};
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&p.counters[wid], 1) == p.split - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dkt[db][r] = 0.f;
-        dvt[db][r] = 0.f;
-      }
-    for (int sl = 0; sl < p.split; ++sl) {
-      const float* qk = p.part + (size_t)sl * 2 * p.part_half;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4_t xk = *reinterpret_cast<const f32x4_t*>(qk + poff + 32 * db + 8 * r4);
-          const f32x4_t xv =
-              *reinterpret_cast<const f32x4_t*>(qk + p.part_half + poff + 32 * db + 8 * r4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dkt[db][4 * r4 + e] += xk[e];
-            dvt[db][4 * r4 + e] += xv[e];
-          }
-        }
-    }
+    return;
   }
 
   if constexpr (ACC) {
@@ -409,6 +373,38 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
       *reinterpret_cast<u32x4_t*>(p.dk + off) = vk;
       *reinterpret_cast<u32x4_t*>(p.dv + off) = vv;
     }
+  }
+}
+
+// Sum of the split dK/dV partials, slice 0 first (the order does not depend
+// on scheduling, so results are bitwise repeatable), then the epilogue: dK =
+// scale sum, dV = sum, written as bf16 or (ACC) added to the fp32
+// accumulators.  Four elements per thread, consecutive in memory.
+template <bool ACC>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce(BwdParams p) {
+  const long long n4 = (long long)(p.part_half / 4);
+  const long long e = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= n4) return;
+  f32x4_t sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < p.split; ++sl) {
+    const float* pk = p.part + (size_t)sl * 2 * p.part_half;
+    sk = sk + reinterpret_cast<const f32x4_t*>(pk)[e];
+    sv = sv + reinterpret_cast<const f32x4_t*>(pk + p.part_half)[e];
+  }
+  sk = sk * p.scale;
+  if constexpr (ACC) {
+    f32x4_t* dk = reinterpret_cast<f32x4_t*>(p.dk_acc) + e;
+    f32x4_t* dv = reinterpret_cast<f32x4_t*>(p.dv_acc) + e;
+    *dk = *dk + sk;
+    *dv = *dv + sv;
+  } else {
+    u32x2_t wk, wv;
+    wk[0] = pack_bf16x2(sk[0], sk[1]);
+    wk[1] = pack_bf16x2(sk[2], sk[3]);
+    wv[0] = pack_bf16x2(sv[0], sv[1]);
+    wv[1] = pack_bf16x2(sv[2], sv[3]);
+    reinterpret_cast<u32x2_t*>(p.dk)[e] = wk;
+    reinterpret_cast<u32x2_t*>(p.dv)[e] = wv;
   }
 }
 
@@ -625,8 +621,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
 
 // dK/dV workgroups per (key tile, key/value head) pair: when the key tiles
 // alone give fewer than two workgroups per CU, the query steps of each key
-// tile are split over up to four workgroups whose partial sums are added
-// deterministically by the last one to finish.
+// tile are split over up to four workgroups, whose partial sums a second
+// kernel adds up in a fixed order.
 constexpr int kDkdvTargetWGs = 512;
 
 int dkdv_split(int n, int l_k, int h_kv) {
@@ -636,11 +632,11 @@ int dkdv_split(int n, int l_k, int h_kv) {
 }
 
 // Workspace layout: D and LSE2 per query row, then (split > 1) the per-slice
-// dK, dV partials and the arrival counters, each part 256-byte aligned.
+// dK, dV partials, each part 256-byte aligned.
 struct BwdWorkspace {
-  size_t dd, lse2, part, counters, total;
+  size_t dd, lse2, part, total;
   size_t part_half;  // floats in one partial dK (or dV)
-  int split, n_counters;
+  int split;
 };
 
 BwdWorkspace bwd_layout(int n, int l_q, int l_k, int h, int h_kv, int d) {
@@ -648,13 +644,11 @@ BwdWorkspace bwd_layout(int n, int l_q, int l_k, int h, int h_kv, int d) {
   BwdWorkspace w;
   const size_t rows = (size_t)n * l_q * h;
   w.split = dkdv_split(n, l_k, h_kv);
-  w.n_counters = w.split > 1 ? ((l_k + kKeysPerWG - 1) / kKeysPerWG) * n * h_kv : 0;
   w.part_half = w.split > 1 ? (size_t)n * l_k * h_kv * d : 0;
   w.dd = 0;
   w.lse2 = up(rows * 4);
   w.part = w.lse2 + up(rows * 4);
-  w.counters = w.part + up((size_t)w.split * 2 * w.part_half * 4 * (w.split > 1));
-  w.total = w.counters + up((size_t)w.n_counters * 4);
+  w.total = w.part + up((size_t)w.split * 2 * w.part_half * 4);
   return w;
 }
 
@@ -668,6 +662,11 @@ hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, ACC>),
                      dim3((unsigned)(p.split * n_ktiles * p.n * p.h_kv)), dim3(kThreads),
                      0, stream, p, n_ktiles, causal ? 1 : 0);
+  if (p.split > 1) {
+    const long long n4 = (long long)(p.part_half / 4);
+    hipLaunchKernelGGL((bwd_dkdv_reduce<ACC>), dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, p);
+  }
   const int n_qtiles = (p.l_q + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_kernel<D, ACC>), dim3((unsigned)(n_qtiles * p.n * p.h)),
                      dim3(kThreads), 0, stream, p, n_qtiles, causal ? 1 : 0);
@@ -705,8 +704,6 @@ hipError_t launch_bwd(const void* dout, const void* q, const void* k,
   p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   p.part = reinterpret_cast<float*>(ws + w.part);
   p.part_half = w.part_half;
-  p.counters = reinterpret_cast<int*>(ws + w.counters);
-  p.n_counters = w.n_counters;
   p.split = w.split;
   p.n = s.n;
   p.l_q = s.l_q;

@@ -208,8 +208,7 @@ int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
 /* Bytes of workspace attn_bwd / attn_bwd_acc need for these sizes (0 on
  * invalid sizes): D and LSE per query row and, when the key tiles alone would
  * give the dK/dV kernel fewer than 512 workgroups, per-split float32 dK/dV
- * partials and arrival counters (the splits are summed in a fixed order, so
- * results stay bitwise repeatable). */
+ * partials (summed in a fixed order, so results stay bitwise repeatable). */
 size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);
 
 /* Static, human-readable name of a status code. */
