@@ -9,7 +9,8 @@
 // it.  Gradients are written in the input dtype ("flash_sharding.py",
 // ring_bwd casts them to q's dtype).
 //
-// Three kernels, no atomics (results are bitwise repeatable):
+// Three kernels (four when the dK/dV grid is split), no atomics, results
+// bitwise repeatable:
 //  * bwd_pre: D_i and LSE_i * log2(e) per query row (+inf for a row with no
 //    allowed key, so its P is exactly 0), into the workspace.
 //  * bwd_dkdv: one workgroup per 128 keys of one key/value head, 32 keys per
@@ -22,8 +23,11 @@
 //    (B operands); key tiles stream through LDS.  S^T = K Q^T and
 //    dP^T = V dO^T put one query per lane, so dQ^T += K^T dS^T reads dS^T
 //    straight from registers; K^T is read transposed out of the K tile.
-// Tiles use the layout of the forward kernel (swizzled rows, direct loads,
-// two buffers one tile ahead).
+//  * bwd_dkdv_reduce (small dK/dV grids only): the sum of the per-slice dK,
+//    dV partials, in slice order.
+// The ACC instantiations add the gradients to float32 accumulators instead of
+// writing them (one step of the ring backward).  Tiles use the layout of the
+// forward kernel (swizzled rows, direct loads, two buffers one tile ahead).
 #include <algorithm>
 
 #include "common.hpp"

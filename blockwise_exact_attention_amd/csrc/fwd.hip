@@ -25,6 +25,8 @@
 //    visited; tiles wholly inside run without per-element mask work.
 //  * The normalised O rows leave through LDS, so that each global store
 //    writes whole rows rather than 16-byte pieces of 32 rows.
+//  * The ACC instantiations (one fused ring step) merge (O, LSE) into a
+//    float32 accumulator in the epilogue instead of writing them.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
