@@ -275,27 +275,33 @@ class RingShareBwd:
         self.window = (int(window[0]), int(window[1]))
         self.dq_acc = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         self.dq = torch.empty_like(q)
+        self.kv_acc = None
         self.dk_acc = []
         self.dv_acc = []
         self.ws = None
 
     def run(self, k_chunks, v_chunks, k_offsets, stream=None):
         n, l_q, h, d = self.q.shape
-        if len(self.dk_acc) != len(k_chunks):
-            self.dk_acc = [torch.empty(kc.shape, dtype=torch.float32,
-                                       device=kc.device) for kc in k_chunks]
-            self.dv_acc = [torch.empty(kc.shape, dtype=torch.float32,
-                                       device=kc.device) for kc in k_chunks]
+        P = len(k_chunks)
+        shape = tuple(k_chunks[0].shape)
+        if len(self.dk_acc) != P or tuple(self.dk_acc[0].shape) != shape:
+            # all chunks' (dK, dV) accumulators in one buffer, zeroed by a
+            # single launch per run
+            self.kv_acc = torch.empty((2 * P * shape[0],) + shape[1:],
+                                      dtype=torch.float32, device=self.q.device)
+            self.dk_acc = [self.kv_acc[s * shape[0]:(s + 1) * shape[0]]
+                           for s in range(P)]
+            self.dv_acc = [self.kv_acc[(P + s) * shape[0]:(P + s + 1) * shape[0]]
+                           for s in range(P)]
         if self.ws is None:
-            _, l_k, h_kv, _ = k_chunks[0].shape
+            _, l_k, h_kv, _ = shape
             need = bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d)
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8,
                                   device=self.q.device)
         attn_acc_init(self.dq_acc, None, stream)
+        attn_acc_init(self.kv_acc, None, stream)
         for kc, vc, ko, dka, dva in zip(k_chunks, v_chunks, k_offsets,
                                         self.dk_acc, self.dv_acc):
-            attn_acc_init(dka, None, stream)
-            attn_acc_init(dva, None, stream)
             attn_bwd_acc(self.dout, self.q, kc, vc, self.out, self.lse,
                          self.dq_acc, dka, dva, self.scale, self.causal,
                          self.window[0], self.window[1], self.q_offset, ko,
