@@ -6,14 +6,17 @@ describe the seeded synthetic inputs; `flops` the algorithmic work.
 """
 from .attention import (  # noqa: F401
     attn_fwd,
+    attn_fwd_acc,
     attn_merge,
     attn_acc_init,
     attn_acc_cast,
     attn_bwd,
+    attn_bwd_acc,
     attention_forward,
     attention_backward,
     bwd_workspace_bytes,
     ring_share,
     RingShare,
+    RingShareBwd,
 )
 from ._lib import AttnError, lib  # noqa: F401
