@@ -250,6 +250,8 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
     e2e = timed(lambda: share.run(kc, vc, x["k_offsets"]), steps, 3, torch)
     e2e_fused = timed(lambda: share.run(kc, vc, x["k_offsets"], fused=True),
                       steps, 3, torch)
+    graph = share.capture(kc, vc, x["k_offsets"], fused=True)
+    e2e_graph = timed(graph.replay, steps, 3, torch)
     pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, 7168, 1024 * s)
                 for s in range(8))
     fl = fwd_flops(1, 32, 128, pairs)
@@ -261,6 +263,8 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
                             True, x["q_offset"])
     bwd_ms = timed(lambda: bshare.run(kc, vc, x["k_offsets"]),
                    max(5, steps // 4), 2, torch)
+    bgraph = bshare.capture(kc, vc, x["k_offsets"])
+    bwd_graph_ms = timed(bgraph.replay, max(5, steps // 4), 2, torch)
     mb = merge_bytes(1, 1024, 32, 128, 2)
     res["ring_share_rank7"] = {
         "fwd_tflops_sum_of_8": round(fl / (sum(fwd_ms) * 1e-3) / 1e12, 2),
@@ -270,10 +274,12 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
         "end_to_end_ms": round(e2e, 4),
         "end_to_end_fused_ms": round(e2e_fused, 4),
         "fused_tflops": round(fl / (e2e_fused * 1e-3) / 1e12, 2),
+        "end_to_end_fused_graph_ms": round(e2e_graph, 4),
         "backward_share_ms": round(bwd_ms, 4),
+        "backward_share_graph_ms": round(bwd_graph_ms, 4),
         "backward_share_tflops": round(bwd_flops(1, 32, 128, pairs)
                                        / (bwd_ms * 1e-3) / 1e12, 2)}
-    del bshare, tdo
+    del bgraph, graph, bshare, tdo
     del share, kc, vc, tq
 
     # sliding window

@@ -248,6 +248,25 @@ class RingShare:
         attn_acc_cast(self.acc, self.out, stream)
         return self.out, self.lse_acc
 
+    def capture(self, k_chunks, v_chunks, k_offsets, fused=True):
+        """Record `run` on these chunk buffers into a HIP graph and return it
+        (a torch.cuda.CUDAGraph).  Each replay recomputes the share from what
+        q and the chunk buffers hold at that moment, into the same output
+        buffers; the buffers must outlive the graph."""
+        return _capture(lambda: self.run(k_chunks, v_chunks, k_offsets,
+                                         fused=fused))
+
+
+def _capture(fn):
+    # one eager call first, so that the kernels' code objects are loaded and
+    # every buffer is allocated before the capture
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
 
 def ring_share(q, k_chunks, v_chunks, k_offsets, q_offset, scale=None,
                causal=True, stream=None, fused=False, window=(-1, -1)):
@@ -308,3 +327,7 @@ class RingShareBwd:
                          self.ws, stream)
         attn_acc_cast(self.dq_acc, self.dq, stream)
         return self.dq, self.dk_acc, self.dv_acc
+
+    def capture(self, k_chunks, v_chunks, k_offsets):
+        """Record `run` into a HIP graph (see RingShare.capture)."""
+        return _capture(lambda: self.run(k_chunks, v_chunks, k_offsets))
