@@ -9,7 +9,8 @@ forward TFLOP/s (algorithmic FLOPs: 4*d per allowed query/key pair per head),
 the roofline of the forward kernel, and the fp64 CPU oracle's rate on a
 bounded sample of the same workload.  --extras adds the other workloads
 (ring share with its merges, sliding window, long-context forward and
-backward) as separately timed figures.
+backward, and the merge's bandwidth warm, cold and on a full-sequence shape)
+as separately timed figures; --merge-only runs just the merge figures.
 """
 from __future__ import annotations
 
@@ -38,6 +39,9 @@ def parse():
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--merge-only", action="store_true",
+                    help="only run the merge measurements (warm, cold, full "
+                         "sequence) and print them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 10 times "
                          "(reference for the HBM byte counters) and exit")
@@ -84,11 +88,22 @@ def cpu_baseline(x, w, seconds):
         done += 1
     dt = time.perf_counter() - t0
     flops = fwd_flops(1, done, w.d, pairs)
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else cores
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s",
             "cores": cores, "kind": "oracle",
             "sample": f"{done} (batch, head) forward passes of this workload "
                       f"({done / len(heads_all):.2f} x the whole batch), fp64 "
-                      f"numpy, {dt:.1f} s"}
+                      f"numpy with {cores} BLAS threads, {dt:.1f} s; host "
+                      f"{model}, {os.cpu_count()} logical CPUs, {usable} usable"}
 
 
 KERNEL_SOURCES = ("fwd.hip", "tile.hpp", "common.hpp")
@@ -117,6 +132,69 @@ def counted_traffic():
     if rec.get("kernel_sources_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def merge_measurements(A, torch, merge_bytes, steps):
+    """attn_merge bandwidth on the ring-share shape [1,1024,32,128] (bf16
+    block), warm and cold, and on the full-sequence shape [1,8192,32,128],
+    cold.  Cold: the calls rotate over enough separate buffer sets (403 MB
+    and 606 MB of distinct memory) that each call's data has left the 256 MB
+    Infinity Cache and the L2s since its set was last used, and one event
+    pair spans all the calls (a per-call event pair adds microseconds).
+    Warm: one buffer set, merged into again and again.  A plain device copy
+    (torch), cold the same way, is timed beside them as the reference for
+    what a read-and-write stream reaches on the box."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+
+    def buffers(n, l, h, d):
+        acc = torch.randn((n, l, h, d), generator=gen, device=dev)
+        lacc = torch.randn((n, h, l), generator=gen, device=dev)
+        blk = torch.randn((n, l, h, d), generator=gen, device=dev).to(torch.bfloat16)
+        lblk = torch.randn((n, h, l), generator=gen, device=dev)
+        return acc, lacc, blk, lblk
+
+    def rotating(sets):
+        it = [0]
+
+        def f():
+            A.attn_merge(*sets[it[0] % len(sets)])
+            it[0] += 1
+        return f
+
+    res = {}
+    for name, shape, n_sets, warm in (("ring_block_1x1024x32x128", (1, 1024, 32, 128), 16, True),
+                                      ("full_sequence_1x8192x32x128", (1, 8192, 32, 128), 3, False)):
+        sets = [buffers(*shape) for _ in range(n_sets)]
+        nbytes = merge_bytes(*shape, 2)
+        r = {"bytes": nbytes}
+        if warm:
+            ms = timed(rotating(sets[:1]), steps, 5, torch)
+            r["warm_ms"] = round(ms, 5)
+            r["warm_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        ms = timed(rotating(sets), max(2 * n_sets, steps // n_sets * n_sets),
+                   n_sets, torch)
+        r["cold_ms"] = round(ms, 5)
+        r["cold_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        r["cold_frac_of_hbm"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        res[name] = r
+        del sets
+    # reference: a plain device copy (torch), cold the same way
+    for nb, n_sets in ((32 << 20, 16), (1 << 30, 2)):
+        sets = [(torch.ones(nb // 4, device=dev), torch.empty(nb // 4, device=dev))
+                for _ in range(n_sets)]
+        it = [0]
+
+        def copy():
+            src, dst = sets[it[0] % n_sets]
+            dst.copy_(src)
+            it[0] += 1
+        ms = timed(copy, max(4 * n_sets, 32), n_sets, torch)
+        res[f"copy_{nb >> 20}MiB_cold_gbs"] = round(2 * nb / (ms * 1e-3) / 1e9, 1)
+        del sets
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration(nbytes):
@@ -148,6 +226,10 @@ def main():
                                                      fwd_bytes, bwd_flops,
                                                      merge_bytes)
     from blockwise_exact_attention_amd.workloads import WORKLOADS, make_inputs
+    if args.merge_only:
+        print(json.dumps({"merge": merge_measurements(A, torch, merge_bytes,
+                                                      args.steps)}), flush=True)
+        return
 
     w = WORKLOADS["C2"]
     x = make_inputs(w)
@@ -317,6 +399,7 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
     res["long_16k"]["bwd_ms"] = round(msb, 4)
     res["long_16k"]["bwd_tflops"] = round(
         bwd_flops(w.n, w.h, w.d, pairs) / (msb * 1e-3) / 1e12, 2)
+    res["merge"] = merge_measurements(A, torch, merge_bytes, steps)
     return res
 
 
