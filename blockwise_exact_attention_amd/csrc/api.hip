@@ -12,8 +12,11 @@ namespace {
 
 using bea::AttnShape;
 
+// a, b: counts that may be zero (batch, sequence length); c, d: layout
+// sizes that must be positive (heads, head dim).
 bool sizes_ok(long long a, long long b, long long c, long long d) {
-  if (a <= 0 || b <= 0 || c <= 0 || d <= 0) return false;
+  if (a < 0 || b < 0 || c <= 0 || d <= 0) return false;
+  if (a == 0 || b == 0) return true;
   // every element count (and its byte size) must stay far below 2^62
   const long long lim = 1LL << 58;
   if (a > lim / b) return false;
@@ -22,6 +25,9 @@ bool sizes_ok(long long a, long long b, long long c, long long d) {
   const long long abc = ab * c;
   return abc <= lim / d;
 }
+
+// A pointer may be NULL only where its tensor has no elements.
+bool missing(const void* p, long long bytes) { return p == nullptr && bytes > 0; }
 
 bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
@@ -91,26 +97,34 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
              int causal, int win_l, int win_r, long long q_offset,
              long long k_offset, void* stream, int dtype) {
-  if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL;
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
-      !aligned(out, 16) || !aligned(lse, 4))
-    return ATTN_ERR_ALIGN;
   const long long es = dtype == ATTN_BF16 ? 2 : 4;
   const long long qb = (long long)n * l_q * h * d * es;
   const long long kb = (long long)n * l_k * h_kv * d * es;
   const long long lb = (long long)n * h * l_q * 4;
+  if (missing(q, qb) || missing(k, kb) || missing(v, kb) || missing(out, qb) ||
+      missing(lse, lb))
+    return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(out, 16) || !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
   const Range rq = range(q, qb), rk = range(k, kb), rv = range(v, kb),
               ro = range(out, qb), rl = range(lse, lb);
   if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) ||
       overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ro))
     return ATTN_ERR_ALIAS;
+  if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
 
-  AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
-  mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  // no keys: every row is empty, O = 0 and LSE = -inf (O cleared as 32-bit
+  // words: d * es is a multiple of 4)
+  if (kb == 0)
+    return finish(bea::launch_acc_init(static_cast<float*>(out), lse, n, l_q, h,
+                                       (int)(d * es / 4), hs));
+  AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+  mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
   return finish(dtype == ATTN_BF16 ? bea::launch_fwd_bf16(q, k, v, out, lse, s, hs)
                                    : bea::launch_fwd_f32(q, k, v, out, lse, s, hs));
 }
@@ -119,22 +133,27 @@ int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
                  float* lse_acc, int n, int l_q, int l_k, int h, int h_kv, int d,
                  float scale, int causal, int win_l, int win_r,
                  long long q_offset, long long k_offset, void* stream, int dtype) {
-  if (!q || !k || !v || !out_acc || !lse_acc) return ATTN_ERR_NULL;
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
-      !aligned(out_acc, 16) || !aligned(lse_acc, 4))
-    return ATTN_ERR_ALIGN;
   const long long qb = (long long)n * l_q * h * d * 2;
   const long long kb = (long long)n * l_k * h_kv * d * 2;
   const long long ab = (long long)n * l_q * h * d * 4;
   const long long lb = (long long)n * h * l_q * 4;
+  if (missing(q, qb) || missing(k, kb) || missing(v, kb) || missing(out_acc, ab) ||
+      missing(lse_acc, lb))
+    return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(out_acc, 16) || !aligned(lse_acc, 4))
+    return ATTN_ERR_ALIGN;
   const Range rq = range(q, qb), rk = range(k, kb), rv = range(v, kb),
               ra = range(out_acc, ab), rl = range(lse_acc, lb);
   if (overlap(ra, rq) || overlap(ra, rk) || overlap(ra, rv) ||
       overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ra))
     return ATTN_ERR_ALIAS;
+  // no query rows, or an empty chunk (its rows are all empty and merge as
+  // no-ops): the accumulator stays as it is
+  if (qb == 0 || kb == 0) return ATTN_OK;
 
   AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
   mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
@@ -147,20 +166,23 @@ int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
 int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
                const float* lse_blk, int n, int l, int h, int d, int blk_dtype,
                void* stream) {
-  if (!out_acc || !lse_acc || !out_blk || !lse_blk) return ATTN_ERR_NULL;
   if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;
   if (blk_dtype != ATTN_F32 && blk_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(out_acc, 16) || !aligned(out_blk, 16) || !aligned(lse_acc, 4) ||
-      !aligned(lse_blk, 4))
-    return ATTN_ERR_ALIGN;
   const long long es = blk_dtype == ATTN_BF16 ? 2 : 4;
   const long long ne = (long long)n * l * h * d;
   const long long nr = (long long)n * l * h;
+  if (missing(out_acc, ne) || missing(lse_acc, nr) || missing(out_blk, ne) ||
+      missing(lse_blk, nr))
+    return ATTN_ERR_NULL;
+  if (!aligned(out_acc, 16) || !aligned(out_blk, 16) || !aligned(lse_acc, 4) ||
+      !aligned(lse_blk, 4))
+    return ATTN_ERR_ALIGN;
   const Range ra = range(out_acc, ne * 4), rla = range(lse_acc, nr * 4),
               rb = range(out_blk, ne * es), rlb = range(lse_blk, nr * 4);
   if (overlap(ra, rla) || overlap(ra, rb) || overlap(ra, rlb) ||
       overlap(rla, rb) || overlap(rla, rlb))
     return ATTN_ERR_ALIAS;
+  if (nr == 0) return ATTN_OK;
   (void)hipGetLastError();
   return finish(bea::launch_merge(out_acc, lse_acc, out_blk, lse_blk, n, l, h,
                                   d, blk_dtype == ATTN_BF16,
@@ -169,13 +191,14 @@ int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
 
 int attn_acc_init(float* out_acc, float* lse_acc, int n, int l, int h, int d,
                   void* stream) {
-  if (!out_acc) return ATTN_ERR_NULL;  // lse_acc may be NULL: O only
   if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;
-  if (!aligned(out_acc, 4) || !aligned(lse_acc, 4)) return ATTN_ERR_ALIGN;
   const long long ne = (long long)n * l * h * d;
   const long long nr = (long long)n * l * h;
+  if (missing(out_acc, ne)) return ATTN_ERR_NULL;  // lse_acc may be NULL: O only
+  if (!aligned(out_acc, 4) || !aligned(lse_acc, 4)) return ATTN_ERR_ALIGN;
   if (lse_acc && overlap(range(out_acc, ne * 4), range(lse_acc, nr * 4)))
     return ATTN_ERR_ALIAS;
+  if (ne == 0) return ATTN_OK;
   (void)hipGetLastError();
   return finish(bea::launch_acc_init(out_acc, lse_acc, n, l, h, d,
                                      static_cast<hipStream_t>(stream)));
@@ -183,13 +206,14 @@ int attn_acc_init(float* out_acc, float* lse_acc, int n, int l, int h, int d,
 
 int attn_acc_cast(const float* out_acc, void* out, int n, int l, int h, int d,
                   int dtype, void* stream) {
-  if (!out_acc || !out) return ATTN_ERR_NULL;
   if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(out_acc, 16) || !aligned(out, 16)) return ATTN_ERR_ALIGN;
   const long long ne = (long long)n * l * h * d;
   const long long es = dtype == ATTN_BF16 ? 2 : 4;
+  if (missing(out_acc, ne) || missing(out, ne)) return ATTN_ERR_NULL;
+  if (!aligned(out_acc, 16) || !aligned(out, 16)) return ATTN_ERR_ALIGN;
   if (overlap(range(out_acc, ne * 4), range(out, ne * es))) return ATTN_ERR_ALIAS;
+  if (ne == 0) return ATTN_OK;
   (void)hipGetLastError();
   return finish(bea::launch_acc_cast(out_acc, out, n, l, h, d,
                                      dtype == ATTN_BF16,
@@ -200,6 +224,7 @@ size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv,
                                 int d) {
   if (!sizes_ok(n, l_q, h, d) || !sizes_ok(n, l_k, h_kv, d)) return 0;
   if (h % h_kv != 0) return 0;
+  if (n == 0 || l_q == 0 || l_k == 0) return 0;  // nothing is launched
   return bea::bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d);
 }
 
@@ -216,23 +241,27 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
               int causal, int win_l, int win_r, long long q_offset,
               long long k_offset, void* workspace, size_t workspace_bytes,
               void* stream, int dtype, bool acc) {
-  if (!dout || !q || !k || !v || !out || !lse || !dq || !dk || !dv)
-    return ATTN_ERR_NULL;
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  const size_t need = bea::bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) ||
-      !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
-      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(workspace, 16))
-    return ATTN_ERR_ALIGN;
   const long long es = 2;              // bf16 inputs
   const long long gb = acc ? 4 : es;   // gradient element bytes
   const long long qe = (long long)n * l_q * h * d;
   const long long ke = (long long)n * l_k * h_kv * d;
   const long long lb = (long long)n * h * l_q * 4;
+  if (missing(dout, qe) || missing(q, qe) || missing(k, ke) || missing(v, ke) ||
+      missing(out, qe) || missing(lse, lb) || missing(dq, qe) || missing(dk, ke) ||
+      missing(dv, ke))
+    return ATTN_ERR_NULL;
+  const bool empty = qe == 0 || ke == 0;
+  const size_t need = empty ? 0 : bea::bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d);
+  if (missing(workspace, (long long)need) || workspace_bytes < need)
+    return ATTN_ERR_WORKSPACE;
+  if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) ||
+      !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(workspace, 16))
+    return ATTN_ERR_ALIGN;
   const Range ins[] = {range(dout, qe * es), range(q, qe * es), range(k, ke * es),
                        range(v, ke * es), range(out, qe * es), range(lse, lb)};
   const Range outs[] = {range(dq, qe * gb), range(dk, ke * gb), range(dv, ke * gb),
@@ -243,10 +272,25 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
     for (int c = a + 1; c < 4; ++c)
       if (overlap(outs[a], outs[c])) return ATTN_ERR_ALIAS;
   }
-  AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
-  mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
   (void)hipGetLastError();
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (empty) {
+    // No queries or no keys: every gradient is zero.  The accumulating form
+    // adds nothing; the plain form clears the non-empty gradients (as 32-bit
+    // words: d * gb is a multiple of 4).
+    if (acc || (qe == 0 && ke == 0)) return ATTN_OK;
+    if (qe == 0) {
+      hipError_t e = bea::launch_acc_init(static_cast<float*>(dk), nullptr, n, l_k,
+                                          h_kv, (int)(d * gb / 4), hs);
+      if (e != hipSuccess) return ATTN_ERR_HIP;
+      return finish(bea::launch_acc_init(static_cast<float*>(dv), nullptr, n, l_k,
+                                         h_kv, (int)(d * gb / 4), hs));
+    }
+    return finish(bea::launch_acc_init(static_cast<float*>(dq), nullptr, n, l_q, h,
+                                       (int)(d * gb / 4), hs));
+  }
+  AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+  mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
   if (acc)
     return finish(bea::launch_bwd(dout, q, k, v, out, lse, nullptr, nullptr, nullptr,
                                   s, workspace, true, hs, static_cast<float*>(dq),
@@ -284,8 +328,8 @@ int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
-    case ATTN_ERR_NULL: return "a required pointer is NULL";
-    case ATTN_ERR_SHAPE: return "invalid sizes (<= 0, h % h_kv != 0, or too large)";
+    case ATTN_ERR_NULL: return "a pointer to a non-empty tensor is NULL";
+    case ATTN_ERR_SHAPE: return "invalid sizes (negative, h, h_kv or d <= 0, h % h_kv != 0, or too large)";
     case ATTN_ERR_UNSUPPORTED: return "unsupported head dim, dtype or scale";
     case ATTN_ERR_HIP: return "HIP launch failure";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";

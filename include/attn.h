@@ -42,6 +42,14 @@
  *     matters.  Offsets 0 give top-left causal alignment.
  *   - A query row with no allowed key gets O = 0 and LSE = -inf, and zero
  *     gradients.
+ *   - Empty inputs: n, l_q, l_k (and l of the accumulator calls) may be 0;
+ *     h, h_kv and d may not.  A pointer may be NULL exactly when its tensor
+ *     has no elements.  With no query rows a call writes nothing; with no
+ *     keys (l_k = 0) every row is empty: attn_fwd writes O = 0 and
+ *     LSE = -inf, attn_fwd_acc leaves the accumulator as it is (an empty
+ *     chunk merges as a no-op), attn_bwd writes dQ = 0 (and dK = dV = 0 when
+ *     l_q = 0 instead), attn_bwd_acc adds nothing.  These are the pages'
+ *     fully-masked conventions applied to a chunk with no rows or no keys.
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Every
  *     call only enqueues work on it and returns without synchronising.  The
  *     library keeps no global state: calls on different streams from
@@ -61,12 +69,14 @@ extern "C" {
 
 enum attn_status {
   ATTN_OK = 0,
-  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                        */
-  ATTN_ERR_SHAPE = 2,       /* a size is <= 0, h % h_kv != 0, or sizes overflow  */
+  ATTN_ERR_NULL = 1,        /* a pointer to a non-empty tensor is NULL           */
+  ATTN_ERR_SHAPE = 2,       /* a size is negative, h, h_kv or d is 0,
+                               h % h_kv != 0, or sizes overflow                  */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite
                                scale, or fp32 backward / fused ring step         */
   ATTN_ERR_HIP = 4,         /* the HIP runtime reported a launch failure         */
-  ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
+  ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than required (or NULL when
+                               required)                                         */
   ATTN_ERR_ALIAS = 6,       /* an input buffer overlaps an output buffer         */
   ATTN_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned (LSE
                                pointers: 4-byte aligned)                          */
@@ -206,7 +216,8 @@ int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
                  void* workspace, size_t workspace_bytes, void* stream, int dtype);
 
 /* Bytes of workspace attn_bwd / attn_bwd_acc need for these sizes (0 on
- * invalid sizes): D and LSE per query row and, when the key tiles alone would
+ * invalid sizes, and 0 when n, l_q or l_k is 0: then no kernel reads it and
+ * workspace may be NULL): D and LSE per query row and, when the key tiles alone would
  * give the dK/dV kernel fewer than 512 workgroups, per-split float32 dK/dV
  * partials (summed in a fixed order, so results stay bitwise repeatable). */
 size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);

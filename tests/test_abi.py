@@ -99,11 +99,45 @@ def test_fwd_null(field):
     assert _fwd(**{field: None}) == ATTN_ERR_NULL
 
 
-@pytest.mark.parametrize("kw", [dict(n=0), dict(l_q=0), dict(l_k=-1),
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(l_q=-1), dict(l_k=-1),
                                 dict(h=0), dict(h_kv=0), dict(h=6, h_kv=4),
                                 dict(d=0), dict(n=1 << 30, l_q=1 << 30)])
 def test_fwd_shape(kw):
     assert _fwd(**kw) == ATTN_ERR_SHAPE
+
+
+def test_empty_inputs_need_no_pointers_and_launch_nothing():
+    """Zero rows (n = 0 or l_q = 0), or an empty chunk for the calls that then
+    leave their outputs alone, return ATTN_OK before any HIP call, with NULL
+    for every tensor that has no elements.  A NULL pointer to a non-empty
+    tensor is still an error."""
+    L = _lib.lib()
+    nul = dict(q=None, k=None, v=None, out=None, lse=None)
+    assert _fwd(n=0, **nul) == ATTN_OK
+    assert _fwd(l_q=0, l_k=0, **nul) == ATTN_OK
+    assert _fwd(l_q=0, q=None, out=None, lse=None) == ATTN_OK
+    assert _fwd(l_k=0, k=None, v=None, out=None) == ATTN_ERR_NULL   # O has rows
+    assert _fwd(n=0, h=0, **nul) == ATTN_ERR_SHAPE
+    assert _fwd_acc(l_q=0, q=None, acc=None, lse=None) == ATTN_OK
+    assert _fwd_acc(l_k=0, k=None, v=None) == ATTN_OK   # empty chunk: no-op
+    assert _fwd_acc(l_k=0, k=None, v=None, acc=None) == ATTN_ERR_NULL
+    assert L.attn_merge(None, None, None, None, 1, 0, 2, 64, ATTN_BF16, None) == ATTN_OK
+    assert L.attn_merge(None, None, None, None, 0, 5, 2, 64, ATTN_BF16, None) == ATTN_OK
+    assert L.attn_merge(A, B, None, D_, 1, 5, 2, 64, ATTN_BF16, None) == ATTN_ERR_NULL
+    assert L.attn_acc_init(None, None, 0, 5, 2, 64, None) == ATTN_OK
+    assert L.attn_acc_cast(None, None, 3, 0, 2, 64, ATTN_BF16, None) == ATTN_OK
+    for sizes in ((0, 128, 128), (1, 0, 128), (1, 128, 0)):
+        assert L.attn_bwd_workspace_bytes(*sizes, 2, 2, 64) == 0
+    bwd_args = lambda n, l_q, l_k, ptrs: (*ptrs, n, l_q, l_k, 2, 2, 64, 0.125, 1,
+                                          -1, -1, 0, 0, None, 0, None, ATTN_BF16)
+    assert L.attn_bwd(*bwd_args(0, 128, 128, [None] * 9)) == ATTN_OK
+    assert L.attn_bwd(*bwd_args(1, 0, 0, [None] * 9)) == ATTN_OK
+    # accumulating backward with no keys or no queries adds nothing
+    kv_none = [A, A + (1 << 28), None, None, C, C + (1 << 28), D_, None, None]
+    assert L.attn_bwd_acc(*bwd_args(1, 128, 0, kv_none)) == ATTN_OK
+    q_none = [None, None, B, B + (1 << 28), None, None, None, D_, D_ + (1 << 28)]
+    assert L.attn_bwd_acc(*bwd_args(1, 0, 128, q_none)) == ATTN_OK
+    assert L.attn_bwd(*bwd_args(1, 128, 0, kv_none[:6] + [None] * 3)) == ATTN_ERR_NULL
 
 
 @pytest.mark.parametrize("kw", [dict(d=96), dict(d=256), dict(dtype=7),
@@ -136,7 +170,8 @@ def test_merge_checks():
                             x["h"], x["d"], x["dt"], None)
     assert call(a=None) == ATTN_ERR_NULL
     assert call(lb=None) == ATTN_ERR_NULL
-    assert call(l=0) == ATTN_ERR_SHAPE
+    assert call(l=-1) == ATTN_ERR_SHAPE
+    assert call(h=0) == ATTN_ERR_SHAPE
     assert call(dt=3) == ATTN_ERR_UNSUPPORTED
     assert call(a=A + 4) == ATTN_ERR_ALIGN
     assert call(b=A + 16) == ATTN_ERR_ALIAS
