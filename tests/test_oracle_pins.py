@@ -497,6 +497,34 @@ def test_backward_fully_masked_rows_have_zero_grads():
     assert np.all(dq == 0.0) and np.all(dk == 0.0) and np.all(dv == 0.0)
 
 
+def test_empty_sequences():
+    """No keys: every row is fully masked (O = 0, LSE = -inf, dQ = 0); no
+    query rows: dK = dV = 0; and a chunk with no keys merges as a no-op, so
+    the ring share is unchanged by it."""
+    rng = np.random.default_rng(31)
+    q = _rand(rng, 1, 5, 2, 3)
+    do = _rand(rng, 1, 5, 2, 3)
+    k0 = np.zeros((1, 0, 2, 3))
+    o, lse = oracle.attention_fwd(q, k0, k0, 1.0, True)
+    assert o.shape == q.shape and np.all(o == 0.0) and np.all(np.isneginf(lse))
+    dq, dk, dv = oracle.attention_bwd(q, k0, k0, do, 1.0, True)
+    assert np.all(dq == 0.0) and dk.shape == (1, 0, 2, 3)
+    k = _rand(rng, 1, 6, 2, 3)
+    v = _rand(rng, 1, 6, 2, 3)
+    q0 = np.zeros((1, 0, 2, 3))
+    dq, dk, dv = oracle.attention_bwd(q0, k, v, q0, 1.0, True)
+    assert np.all(dk == 0.0) and np.all(dv == 0.0)
+    full = oracle.ring_share(q, [k[:, :3], k[:, 3:]], [v[:, :3], v[:, 3:]], 1.0,
+                             True, 3, [0, 3])
+    with_empty = oracle.ring_share(q, [k[:, :3], k0, k[:, 3:]],
+                                   [v[:, :3], k0, v[:, 3:]], 1.0, True, 3,
+                                   [0, 3, 3])
+    for a, b in zip(full, with_empty):
+        assert np.array_equal(a, b)
+    ref_o, ref_l = brute_attention(q, k, v, 1.0, True, -1, -1, 3, 0)
+    assert np.allclose(full[0], ref_o, atol=1e-12)
+
+
 # ---------------------------------------------------------------- pins bite
 
 def test_pins_catch_planted_mistakes():
