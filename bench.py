@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="only time the fp64 oracle on every workload at its "
+                         "full size on the host cores and print the times")
     ap.add_argument("--merge-only", action="store_true",
                     help="only run the merge measurements (warm, cold, full "
                          "sequence) and print them")
@@ -88,22 +91,14 @@ def cpu_baseline(x, w, seconds):
         done += 1
     dt = time.perf_counter() - t0
     flops = fwd_flops(1, done, w.d, pairs)
-    model = "unknown CPU"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else cores
+    host = _host_description()
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s",
             "cores": cores, "kind": "oracle",
             "sample": f"{done} (batch, head) forward passes of this workload "
                       f"({done / len(heads_all):.2f} x the whole batch), fp64 "
                       f"numpy with {cores} BLAS threads, {dt:.1f} s; host "
-                      f"{model}, {os.cpu_count()} logical CPUs, {usable} usable"}
+                      f"{host['model']}, {host['logical_cpus']} logical CPUs, "
+                      f"{host['usable_cpus']} usable"}
 
 
 KERNEL_SOURCES = ("fwd.hip", "tile.hpp", "common.hpp")
@@ -197,6 +192,72 @@ def merge_measurements(A, torch, merge_bytes, steps):
     return res
 
 
+def oracle_times():
+    """Wall time of the fp64 oracle (as it stands) on each workload at full
+    size on this host's cores: best of 3 for the small ones, one run for the
+    causal 2048- and 16384-token ones (forward, and forward plus backward for
+    the latter).  Input generation is not timed."""
+    import oracle
+    from blockwise_exact_attention_amd.flops import (allowed_pairs, bwd_flops,
+                                                     fwd_flops)
+    from blockwise_exact_attention_amd.workloads import WORKLOADS, make_inputs
+    res = {"cpu": _host_description()}
+    for name, w in WORKLOADS.items():
+        x = make_inputs(w)
+        reps = 1 if name in ("C2", "C5") else 3
+        if w.ring_chunks:
+            def fwd():
+                oracle.ring_share(x["q"], x["k_chunks"], x["v_chunks"],
+                                  w.softmax_scale, True, x["q_offset"],
+                                  x["k_offsets"])
+            pairs = sum(allowed_pairs(w.l_q, w.l_k, True, -1, -1, x["q_offset"], ko)
+                        for ko in x["k_offsets"])
+        else:
+            def fwd():
+                oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale,
+                                     w.causal, w.win_l, w.win_r)
+            pairs = allowed_pairs(w.l_q, w.l_k, w.causal, w.win_l, w.win_r)
+        best = math.inf
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fwd()
+            best = min(best, time.perf_counter() - t0)
+        r = {"fwd_s": round(best, 3), "runs": reps,
+             "fwd_tflops": round(fwd_flops(w.n, w.h, w.d, pairs) / best / 1e12, 5)}
+        if w.backward:
+            t0 = time.perf_counter()
+            oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], w.softmax_scale,
+                                 w.causal, w.win_l, w.win_r)
+            tb = time.perf_counter() - t0
+            r["bwd_s"] = round(tb, 3)
+            r["bwd_tflops"] = round(bwd_flops(w.n, w.h, w.d, pairs) / tb / 1e12, 5)
+        res[name] = r
+        print(json.dumps({name: r}), file=sys.stderr, flush=True)
+    return res
+
+
+def _host_description():
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = os.cpu_count() or 1
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [threads])
+    except Exception:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else threads
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable,
+            "blas_threads": threads}
+
+
 def copy_calibration(nbytes):
     """A plain device-to-device copy of nbytes, ten times: the reference that
     the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
@@ -219,6 +280,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.oracle_times:
+        print(json.dumps({"oracle_times": oracle_times()}), flush=True)
         return
     import torch
     from blockwise_exact_attention_amd import attention as A
