@@ -219,16 +219,35 @@ def oracle_times():
             pairs = allowed_pairs(w.l_q, w.l_k, w.causal, w.win_l, w.win_r)
         best = math.inf
         for _ in range(reps):
-            t0 = time.perf_counter()
-            fwd()
-            best = min(best, time.perf_counter() - t0)
+            if w.backward:
+                # the long workload head by head (the oracle treats heads
+                # independently), with a progress line per head
+                t = 0.0
+                for hq in range(w.h):
+                    t0 = time.perf_counter()
+                    oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale,
+                                         w.causal, w.win_l, w.win_r,
+                                         heads=[(b, hq) for b in range(w.n)])
+                    t += time.perf_counter() - t0
+                    print(f"{name} forward head {hq}: {t:.1f} s", file=sys.stderr,
+                          flush=True)
+            else:
+                t0 = time.perf_counter()
+                fwd()
+                t = time.perf_counter() - t0
+            best = min(best, t)
         r = {"fwd_s": round(best, 3), "runs": reps,
              "fwd_tflops": round(fwd_flops(w.n, w.h, w.d, pairs) / best / 1e12, 5)}
         if w.backward:
-            t0 = time.perf_counter()
-            oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], w.softmax_scale,
-                                 w.causal, w.win_l, w.win_r)
-            tb = time.perf_counter() - t0
+            tb = 0.0
+            for g in range(w.h_kv):
+                t0 = time.perf_counter()
+                oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], w.softmax_scale,
+                                     w.causal, w.win_l, w.win_r,
+                                     kv_heads=[(b, g) for b in range(w.n)])
+                tb += time.perf_counter() - t0
+                print(f"{name} backward head {g}: {tb:.1f} s", file=sys.stderr,
+                      flush=True)
             r["bwd_s"] = round(tb, 3)
             r["bwd_tflops"] = round(bwd_flops(w.n, w.h, w.d, pairs) / tb / 1e12, 5)
         res[name] = r
