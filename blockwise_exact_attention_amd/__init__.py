@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     attn_bwd_acc,
     attention_forward,
     attention_backward,
+    flash_attention,
     bwd_workspace_bytes,
     ring_share,
     RingShare,

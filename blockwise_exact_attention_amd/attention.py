@@ -211,6 +211,43 @@ def attention_backward(dout, q, k, v, out, lse, scale=None, causal=False,
                     window[0], window[1], q_offset, k_offset, None, stream)
 
 
+class _Attention(torch.autograd.Function):
+    """attn_fwd as the forward and attn_bwd as the backward of one autograd
+    node (the pages' custom_vjp pairing of the kernel's fwd and bwd).  The
+    node keeps q, k, v, O and LSE for the backward; LSE is returned as a
+    non-differentiable output."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal, window, q_offset, k_offset):
+        o, lse = attention_forward(q, k, v, scale, causal, window, q_offset,
+                                   k_offset)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (scale, causal, window, q_offset, k_offset)
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        scale, causal, window, q_offset, k_offset = ctx.args
+        dq, dk, dv = attention_backward(do.contiguous(), q, k, v, o, lse, scale,
+                                        causal, window, q_offset, k_offset)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def flash_attention(q, k, v, scale=None, causal=False, window=(-1, -1),
+                    q_offset=0, k_offset=0, return_lse=False):
+    """Differentiable exact attention: O (and LSE with return_lse) from
+    attn_fwd, gradients of q, k, v from attn_bwd (bf16 only for the
+    backward).  scale defaults to 1/sqrt(d)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o, lse = _Attention.apply(q, k, v, float(scale), bool(causal),
+                              (int(window[0]), int(window[1])), int(q_offset),
+                              int(k_offset))
+    return (o, lse) if return_lse else o
+
+
 class RingShare:
     """One device's share of ring attention, with its buffers allocated once:
     the float32 accumulator (O, LSE), one block (O, LSE) per step and the

@@ -193,3 +193,32 @@ def test_c3_ring_share_backward():
     for s in (0, 3, 7):
         check_grad(host(dk_acc[s]), rk[:, s * c:(s + 1) * c], f"C3 chunk {s} dk")
         check_grad(host(dv_acc[s]), rv[:, s * c:(s + 1) * c], f"C3 chunk {s} dv")
+
+
+@pytest.mark.parametrize("causal,window,h_kv", [(True, (-1, -1), 2), (True, (40, 0), 1),
+                                                (False, (-1, -1), 4)])
+def test_flash_attention_autograd(causal, window, h_kv):
+    """flash_attention under torch autograd: the forward equals attn_fwd, the
+    gradients torch computes through the node equal attn_bwd's bit for bit,
+    and both match the oracle."""
+    q, k, v, do = (round_to_bf16(x) for x in draw_normal(
+        811, [(1, 200, 4, 128), (1, 230, h_kv, 128), (1, 230, h_kv, 128),
+              (1, 200, 4, 128)]))
+    tq, tk, tv, tdo = (dev(x, "bf16") for x in (q, k, v, do))
+    for t in (tq, tk, tv):
+        t.requires_grad_(True)
+    o = A.flash_attention(tq, tk, tv, 0.09, causal, window)
+    (o.float() * tdo.float()).sum().backward()
+    with torch.no_grad():
+        o_ref, lse_ref = A.attention_forward(tq, tk, tv, 0.09, causal, window)
+        g_ref = A.attention_backward(tdo, tq, tk, tv, o_ref, lse_ref, 0.09, causal,
+                                     window)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref)
+    for g, r in zip((tq.grad, tk.grad, tv.grad), g_ref):
+        assert torch.equal(g, r)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, 0.09, causal, window[0],
+                                      window[1])
+    check_grad(host(tq.grad), rq, "autograd dq")
+    check_grad(host(tk.grad), rk, "autograd dk")
+    check_grad(host(tv.grad), rv, "autograd dv")
