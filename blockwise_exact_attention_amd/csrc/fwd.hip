@@ -8,7 +8,9 @@
 // no allowed key gives O = 0 and LSE = -inf; the log1p merge, which the
 // online softmax applies per key tile).
 //
-// bf16 kernel layout (one workgroup = 4 waves = 128 query rows of one head):
+// bf16 kernel layout (one key group = 4 waves = 128 query rows of one head;
+// a workgroup holds one key group, or two that split the key tiles, see
+// KSPLIT below):
 //  * Each wave owns 32 query rows.  Scores are computed transposed,
 //    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows come from LDS as the
 //    A operand, the wave's Q rows stay in VGPRs as the B operand for the whole
