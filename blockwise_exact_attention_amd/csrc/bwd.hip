@@ -423,9 +423,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce(BwdParams p) {
 // K^T read transposed out of the row-major K tile reads dS^T straight from
 // registers as its B operand.
 
-template <int D, bool ACC>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_qtiles,
-                                                             int reverse) {
+template <int D, bool ACC, int KSPLIT>
+__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq_kernel(
+    BwdParams p, int n_qtiles, int reverse) {
   constexpr int BN = 64;
   constexpr int RB = D * 2;
   constexpr int TB = BN * RB;
@@ -435,14 +435,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
   constexpr int NPS = BN / 16;
   constexpr int BM = 128;
   constexpr uint32_t kVC = D == 128 ? 32u : 16u;
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TB];
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TB];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TB];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[KSPLIT][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[KSPLIT][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[KSPLIT][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[KSPLIT][TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = KSPLIT == 1 ? 0 : wave_all / 4;         // key group
+  const int wave = KSPLIT == 1 ? wave_all : wave_all % 4;  // query block of this wave
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
   }
   auto step = [&](int kt, const unsigned char* kl, const unsigned char* vl, unsigned char* kn,
                   unsigned char* vn) {
-    if (kt + 1 < kt_end) load(kt + 1, kn, vn);
+    if (kt + KSPLIT < kt_end) load(kt + KSPLIT, kn, vn);
     const int j0 = kt * BN;
     const bool live = wave_live && (long long)j0 <= wjhi && (long long)(j0 + BN - 1) >= wjlo;
     if (live) {
@@ -563,15 +565,57 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads landed
     __syncthreads();
   };
+  // this group's key tiles: kt_begin + grp + KSPLIT u; both groups run the
+  // same number of steps (and barriers), idling past their last tile
+  const int kt_first = kt_begin + grp;
+  const int n_steps = (kt_end - kt_begin + KSPLIT - 1) / KSPLIT;
   if (kt_begin < kt_end) {
-    load(kt_begin, k_lds0, v_lds0);
+    if (kt_first < kt_end) load(kt_first, k_lds0[grp], v_lds0[grp]);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
   // unrolled by two so that every buffer reference is a fixed LDS object
-  for (int kt = kt_begin; kt < kt_end; kt += 2) {
-    step(kt, k_lds0, v_lds0, k_lds1, v_lds1);
-    if (kt + 1 < kt_end) step(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+  if constexpr (KSPLIT == 1) {
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
+      step(kt, k_lds0[0], v_lds0[0], k_lds1[0], v_lds1[0]);
+      if (kt + 1 < kt_end) step(kt + 1, k_lds1[0], v_lds1[0], k_lds0[0], v_lds0[0]);
+    }
+  } else {
+    for (int u = 0; u < n_steps; u += 2) {
+      const int kt = kt_first + KSPLIT * u;
+      if (kt < kt_end) step(kt, k_lds0[grp], v_lds0[grp], k_lds1[grp], v_lds1[grp]);
+      else __syncthreads();
+      if (u + 1 < n_steps) {
+        if (kt + KSPLIT < kt_end)
+          step(kt + KSPLIT, k_lds1[grp], v_lds1[grp], k_lds0[grp], v_lds0[grp]);
+        else __syncthreads();
+      }
+    }
+  }
+  if constexpr (KSPLIT == 2) {
+    // ---- add group 1's partial dQ^T to group 0's through LDS (float4 f =
+    // 4 db + r4 of lane wl at (f, wl), spread over the two V buffers)
+    const int wl = wave * 64 + lane;
+    float4* xo0 = reinterpret_cast<float4*>(&v_lds0[0][0]);
+    float4* xo1 = reinterpret_cast<float4*>(&v_lds1[0][0]);
+    static_assert(NDB * 2 * kThreads * 16 <= KSPLIT * TB, "exchange fits");
+    if (grp == 1) {
+#pragma unroll
+      for (int f = 0; f < 4 * NDB; ++f)
+        (f < 2 * NDB ? xo0 : xo1)[(f % (2 * NDB)) * kThreads + wl] =
+            make_float4(dqt[f / 4][4 * (f % 4)], dqt[f / 4][4 * (f % 4) + 1],
+                        dqt[f / 4][4 * (f % 4) + 2], dqt[f / 4][4 * (f % 4) + 3]);
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int f = 0; f < 4 * NDB; ++f) {
+      const float4 x = (f < 2 * NDB ? xo0 : xo1)[(f % (2 * NDB)) * kThreads + wl];
+      dqt[f / 4][4 * (f % 4)] += x.x;
+      dqt[f / 4][4 * (f % 4) + 1] += x.y;
+      dqt[f / 4][4 * (f % 4) + 2] += x.z;
+      dqt[f / 4][4 * (f % 4) + 3] += x.w;
+    }
   }
 
   if constexpr (ACC) {
@@ -597,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
   uint32_t ln = (uint32_t)lane;
   asm volatile("" : "+v"(ln));
   const uint32_t ecol = ln & 31u, ehalf = ln >> 5;
-  unsigned char* stage = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * 32 * RB;
+  unsigned char* stage = (wave < 2 ? &k_lds0[0][0] : &k_lds1[0][0]) + (wave & 1) * 32 * RB;
   static_assert(2 * 32 * RB <= TB, "staging fits");
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -628,6 +672,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p, int n_
 // tile are split over up to four workgroups, whose partial sums a second
 // kernel adds up in a fixed order.
 constexpr int kDkdvTargetWGs = 512;
+constexpr int kDqCUs = 256;
 
 int dkdv_split(int n, int l_k, int h_kv) {
   const long long w = (long long)((l_k + kKeysPerWG - 1) / kKeysPerWG) * n * h_kv;
@@ -671,9 +716,17 @@ hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkdv_reduce<ACC>), dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, p);
   }
+  // dQ: with fewer than two workgroups per CU, each workgroup's key tiles
+  // are split over two groups of four waves that add their partial dQ at
+  // the end (two waves per SIMD either way)
   const int n_qtiles = (p.l_q + 127) / 128;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, ACC>), dim3((unsigned)(n_qtiles * p.n * p.h)),
-                     dim3(kThreads), 0, stream, p, n_qtiles, causal ? 1 : 0);
+  const long long dq_wgs = (long long)n_qtiles * p.n * p.h;
+  if (dq_wgs < 2 * kDqCUs)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 2>), dim3((unsigned)dq_wgs), dim3(2 * kThreads),
+                       0, stream, p, n_qtiles, causal ? 1 : 0);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 1>), dim3((unsigned)dq_wgs), dim3(kThreads),
+                       0, stream, p, n_qtiles, causal ? 1 : 0);
   return hipGetLastError();
 }
 
