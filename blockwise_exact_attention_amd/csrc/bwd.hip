@@ -22,7 +22,10 @@
 //  * bwd_dq: one workgroup per 128 query rows of one head, Q and dO resident
 //    (B operands); key tiles stream through LDS.  S^T = K Q^T and
 //    dP^T = V dO^T put one query per lane, so dQ^T += K^T dS^T reads dS^T
-//    straight from registers; K^T is read transposed out of the K tile.
+//    straight from registers; K^T is read transposed out of the K tile.  On
+//    a small grid (under two workgroups per CU) a workgroup has two groups
+//    of four waves taking alternate key tiles, whose dQ^T partials are added
+//    through LDS.
 //  * bwd_dkdv_reduce (small dK/dV grids only): the sum of the per-slice dK,
 //    dV partials, in slice order.
 // The ACC instantiations add the gradients to float32 accumulators instead of
@@ -422,6 +425,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce(BwdParams p) {
 // P^T = exp2(c S^T - LSE2), dS^T = P^T (dP^T - D), and dQ^T += K^T dS^T with
 // K^T read transposed out of the row-major K tile reads dS^T straight from
 // registers as its B operand.
+//
+// KSPLIT = 2: eight waves in two groups of four over the same 128 rows, each
+// group with its own LDS buffers and alternate key tiles; dQ is a plain sum
+// over keys, so group 1's partial dQ^T is simply added to group 0's (through
+// LDS) before the epilogue.
 
 template <int D, bool ACC, int KSPLIT>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq_kernel(
