@@ -49,6 +49,14 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(_lib.SIGNATURES)
 
 
+def test_python_constants_match_the_header():
+    text = open(HEADER).read()
+    consts = {m[0]: int(m[1]) for m in re.findall(r"\b(ATTN_\w+)\s*=\s*(\d+)", text)}
+    assert len(consts) == 10
+    for name, value in consts.items():
+        assert getattr(_lib, name) == value, name
+
+
 def test_status_strings():
     for s in range(8):
         assert _lib.status_string(s)
