@@ -417,6 +417,13 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
                       steps, 3, torch)
     graph = share.capture(kc, vc, x["k_offsets"], fused=True)
     e2e_graph = timed(graph.replay, steps, 3, torch)
+    # the all-gather form of the same share: the 8 chunks side by side, one
+    # attn_fwd with the share's absolute query offset
+    kf, vf = t(x["k_full"]), t(x["v_full"])
+    ag_out = torch.empty_like(tq)
+    ag_lse = torch.empty((1, 32, 1024), dtype=torch.float32, device=dev)
+    ag_ms = timed(lambda: A.attn_fwd(tq, kf, vf, ag_out, ag_lse, w.softmax_scale, True,
+                                     -1, -1, x["q_offset"], 0), steps, 3, torch)
     pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, 7168, 1024 * s)
                 for s in range(8))
     fl = fwd_flops(1, 32, 128, pairs)
@@ -440,11 +447,13 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
         "end_to_end_fused_ms": round(e2e_fused, 4),
         "fused_tflops": round(fl / (e2e_fused * 1e-3) / 1e12, 2),
         "end_to_end_fused_graph_ms": round(e2e_graph, 4),
+        "all_gather_share_ms": round(ag_ms, 4),
+        "all_gather_share_tflops": round(fl / (ag_ms * 1e-3) / 1e12, 2),
         "backward_share_ms": round(bwd_ms, 4),
         "backward_share_graph_ms": round(bwd_graph_ms, 4),
         "backward_share_tflops": round(bwd_flops(1, 32, 128, pairs)
                                        / (bwd_ms * 1e-3) / 1e12, 2)}
-    del bgraph, graph, bshare, tdo
+    del bgraph, graph, bshare, tdo, kf, vf, ag_out, ag_lse
     del share, kc, vc, tq
 
     # sliding window

@@ -79,6 +79,10 @@ def test_c3_ring_share():
         o, lse = host(out), host(lse_acc)
         check_o_lse(o, lse, ro, rl, "bf16",
                     f"C3 ring share (fused={fused}) vs full-sequence rows")
+    # the all-gather form: the chunks side by side, one call with the offset
+    o, lse = run_fwd(x["q"], x["k_full"], x["v_full"], "bf16", w.softmax_scale,
+                     True, -1, -1, x["q_offset"], 0)
+    check_o_lse(o, lse, ro, rl, "bf16", "C3 share, all-gathered K/V in one call")
     # the single steps too: step 0 (wholly in the past) and step 7 (diagonal)
     for s in (0, 7):
         ob, lb = run_fwd(x["q"], x["k_chunks"][s], x["v_chunks"][s], "bf16",
