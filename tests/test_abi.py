@@ -2,7 +2,6 @@
 every function the header declares, and rejects bad arguments before making
 any HIP call.  Pointers here are fake addresses: each call must fail its
 argument checks, so nothing is ever dereferenced or launched."""
-import ctypes
 import os
 import re
 

@@ -10,7 +10,7 @@ import torch
 import oracle
 from blockwise_exact_attention_amd import attention as A
 from blockwise_exact_attention_amd.inputs import draw_normal, round_to_bf16
-from gpu_util import TDT, check_o_lse, dev, host, say
+from gpu_util import check_o_lse, dev, host, say
 
 pytestmark = pytest.mark.gpu
 
