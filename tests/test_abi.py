@@ -260,3 +260,25 @@ def test_bwd_acc_checks():
     near = list(ptrs)
     near[7] = D_ + 48 * 1024    # dk_acc inside dq_acc's 64 KiB
     assert call(ptrs=near) == ATTN_ERR_ALIAS
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without libattn.so the binding raises instead of
+    computing anything elsewhere."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libattn.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()
+
+
+def test_host_tensors_are_rejected():
+    """The binding takes device tensors only: host tensors are refused before
+    any library call (there is no CPU path)."""
+    import torch
+    from blockwise_exact_attention_amd import attention as A
+    q = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16)
+    lse = torch.zeros((1, 2, 8))
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_fwd(q, q, q, q.clone(), lse, 0.125)
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_merge(lse.new_zeros((1, 8, 2, 64)), lse.clone(), q, lse)
