@@ -79,8 +79,14 @@ int check_attn_args(int n, int l_q, int l_k, int h, int h_kv, int d,
   if (!sizes_ok(n, l_q, h, d) || !sizes_ok(n, l_k, h_kv, d))
     return ATTN_ERR_SHAPE;
   if (h % h_kv != 0) return ATTN_ERR_SHAPE;
-  // grid size (q tiles x heads) must fit a 32-bit launch
+  // grid sizes (q tiles x heads; split key tiles x key/value heads) must fit
+  // a 32-bit launch
   if ((long long)((l_q + 63) / 64) * n * h > INT_MAX) return ATTN_ERR_SHAPE;
+  if ((long long)((l_k + 63) / 64) * n * h_kv * 4 > INT_MAX) return ATTN_ERR_SHAPE;
+  // the kernels address a 64-row tile with 32-bit offsets from its first
+  // row: a row (h or h_kv heads of d float32 values at most) must stay
+  // below 32 MiB
+  if ((long long)h * d * 4 > (1LL << 25)) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return ATTN_ERR_UNSUPPORTED;

@@ -71,7 +71,9 @@ enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a pointer to a non-empty tensor is NULL           */
   ATTN_ERR_SHAPE = 2,       /* a size is negative, h, h_kv or d is 0,
-                               h % h_kv != 0, or sizes overflow                  */
+                               h % h_kv != 0, sizes overflow, a row of q
+                               (h * d) exceeds 32 MiB in float32, or a grid
+                               would exceed 2^31 workgroups                      */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite
                                scale, or fp32 backward / fused ring step         */
   ATTN_ERR_HIP = 4,         /* the HIP runtime reported a launch failure         */

@@ -108,7 +108,9 @@ def test_fwd_null(field):
 
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(l_q=-1), dict(l_k=-1),
                                 dict(h=0), dict(h_kv=0), dict(h=6, h_kv=4),
-                                dict(d=0), dict(n=1 << 30, l_q=1 << 30)])
+                                dict(d=0), dict(n=1 << 30, l_q=1 << 30),
+                                dict(h=1 << 18, h_kv=1 << 18),
+                                dict(n=1 << 20, l_q=64, l_k=1 << 20, h=64, h_kv=64)])
 def test_fwd_shape(kw):
     assert _fwd(**kw) == ATTN_ERR_SHAPE
 
