@@ -83,6 +83,8 @@ int check_attn_args(int n, int l_q, int l_k, int h, int h_kv, int d,
   // a 32-bit launch
   if ((long long)((l_q + 63) / 64) * n * h > INT_MAX) return ATTN_ERR_SHAPE;
   if ((long long)((l_k + 63) / 64) * n * h_kv * 4 > INT_MAX) return ATTN_ERR_SHAPE;
+  // the backward's row pass launches one workgroup per 16 query rows
+  if ((long long)n * l_q * h > 16LL * INT_MAX) return ATTN_ERR_SHAPE;
   // the kernels address a 64-row tile with 32-bit offsets from its first
   // row: a row (h or h_kv heads of d float32 values at most) must stay
   // below 32 MiB
@@ -173,6 +175,7 @@ int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
                const float* lse_blk, int n, int l, int h, int d, int blk_dtype,
                void* stream) {
   if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;
+  if ((long long)n * l * h > INT_MAX) return ATTN_ERR_SHAPE;  // rows of the merge grid
   if (blk_dtype != ATTN_F32 && blk_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   const long long es = blk_dtype == ATTN_BF16 ? 2 : 4;
   const long long ne = (long long)n * l * h * d;

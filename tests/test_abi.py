@@ -110,7 +110,8 @@ def test_fwd_null(field):
                                 dict(h=0), dict(h_kv=0), dict(h=6, h_kv=4),
                                 dict(d=0), dict(n=1 << 30, l_q=1 << 30),
                                 dict(h=1 << 18, h_kv=1 << 18),
-                                dict(n=1 << 20, l_q=64, l_k=1 << 20, h=64, h_kv=64)])
+                                dict(n=1 << 20, l_q=64, l_k=1 << 20, h=64, h_kv=64),
+                                dict(n=1 << 20, l_q=64, l_k=64, h=1 << 10, h_kv=1)])
 def test_fwd_shape(kw):
     assert _fwd(**kw) == ATTN_ERR_SHAPE
 
@@ -180,6 +181,7 @@ def test_merge_checks():
     assert call(a=None) == ATTN_ERR_NULL
     assert call(lb=None) == ATTN_ERR_NULL
     assert call(l=-1) == ATTN_ERR_SHAPE
+    assert call(n=1 << 12, l=1 << 20, h=1 << 10, d=4) == ATTN_ERR_SHAPE  # 2^42 rows
     assert call(h=0) == ATTN_ERR_SHAPE
     assert call(dt=3) == ATTN_ERR_UNSUPPORTED
     assert call(a=A + 4) == ATTN_ERR_ALIGN
