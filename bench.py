@@ -138,7 +138,7 @@ def merge_measurements(A, torch, merge_bytes, steps):
     pair spans all the calls (a per-call event pair adds microseconds).
     Warm: one buffer set, merged into again and again.  A plain device copy
     (torch), cold the same way, is timed beside them as the reference for
-    what a read-and-write stream reaches on the box."""
+    what a read-and-write stream reaches on this GPU."""
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
@@ -293,8 +293,8 @@ def copy_calibration(nbytes):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); a "
-              "multi-GPU run of this path is not part of this build",
+        print(f"bench.py measures one GPU only (asked for {args.gpus}): the "
+              "path runs on one GPU's share; its multi-GPU form is not provided",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
