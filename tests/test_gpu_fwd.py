@@ -181,6 +181,27 @@ def test_large_offsets():
         check_o_lse(o, lse, ro, rl, "bf16", f"offsets {qo},{ko}")
 
 
+@pytest.mark.parametrize("case", [
+    # n, l_q, l_k, h, h_kv, d, causal, q_offset, rows checked (None = all)
+    (1, 65536, 65536, 1, 1, 64, True, 0, [0, 1, 127, 128, 4095, 32768, 65534, 65535]),
+    (300, 17, 17, 3, 1, 128, False, 0, None),
+    (1, 1, 65536, 4, 2, 128, True, 65535, None),      # one query at the end (decode-like)
+    (1, 65536, 1, 2, 2, 64, True, 0, [0, 1, 2, 65535]),  # one key
+    (2, 129, 40000, 4, 1, 128, True, 39871, None),  # chunk at the end of a long key range
+])
+def test_shape_extremes(case):
+    """Very long and very short sequences, many tiny heads and batches, a
+    single query or key: grid mapping, tile bounds and tails."""
+    n, l_q, l_k, h, h_kv, d, causal, qo, rows = case
+    say(f"[extremes] {case[:8]}")
+    q, k, v = rand_inputs(77, n, l_q, l_k, h, h_kv, d, "bf16")
+    o, lse = run_fwd(q, k, v, "bf16", 0.11, causal, -1, -1, qo, 0)
+    heads = None if rows is None else [(0, 0), (n - 1, h - 1)]
+    ro, rl = oracle.attention_fwd(q, k, v, 0.11, causal, -1, -1, qo, 0, heads=heads,
+                                  rows=rows)
+    check_o_lse(o, lse, ro, rl, "bf16", f"extremes {case[:8]}")
+
+
 # ---------------------------------------------------------------- merge
 
 def _partial(rng, n, l, h, d, p_empty):
