@@ -222,3 +222,25 @@ def test_flash_attention_autograd(causal, window, h_kv):
     check_grad(host(tq.grad), rq, "autograd dq")
     check_grad(host(tk.grad), rk, "autograd dk")
     check_grad(host(tv.grad), rv, "autograd dv")
+
+
+@pytest.mark.parametrize("case", [
+    # n, l_q, l_k, h, h_kv, d, causal, q_offset
+    (300, 17, 17, 3, 1, 128, False, 0),
+    (1, 1, 65536, 4, 2, 128, True, 65535),    # one query against a long key range
+    (1, 20000, 1, 2, 2, 64, True, 0),         # one key seen by every row
+    (2, 129, 40000, 4, 1, 128, True, 39871),  # a short chunk at the end of the keys
+])
+def test_backward_shape_extremes(case):
+    """The backward at shape extremes (many tiny batches, one query, one key,
+    a short query block against a long key range), whole gradients against
+    the oracle."""
+    n, l_q, l_k, h, h_kv, d, causal, qo = case
+    say(f"[bwd extremes] {case}")
+    q, k, v, do = (round_to_bf16(x) for x in draw_normal(
+        91, [(n, l_q, h, d), (n, l_k, h_kv, d), (n, l_k, h_kv, d), (n, l_q, h, d)]))
+    dq, dk, dv = run_fwd_bwd(q, k, v, do, 0.11, causal, -1, -1, qo, 0)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, 0.11, causal, -1, -1, qo, 0)
+    check_grad(dq, rq, f"{case} dq")
+    check_grad(dk, rk, f"{case} dk")
+    check_grad(dv, rv, f"{case} dv")
