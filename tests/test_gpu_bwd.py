@@ -88,6 +88,21 @@ def test_backward_negative_scale():
     check_grad(dv, rv, "dv")
 
 
+@pytest.mark.parametrize("d,window", [(64, (100, 0)), (128, (-1, -1))])
+def test_backward_zero_scale(d, window):
+    # scale 0: every allowed key has the same weight, and dQ = scale dS K,
+    # dK = scale dS^T Q vanish exactly
+    q, k, v, do = draw_normal(7 + d, [(1, 200, 2, d), (1, 200, 1, d),
+                                      (1, 200, 1, d), (1, 200, 2, d)])
+    q, k, v, do = (round_to_bf16(x) for x in (q, k, v, do))
+    dq, dk, dv = run_fwd_bwd(q, k, v, do, 0.0, True, *window)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, 0.0, True, *window)
+    assert not np.any(dq) and not np.any(dk)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
 def test_backward_is_deterministic():
     q, k, v, do = draw_normal(6, [(1, 512, 4, 128), (1, 512, 2, 128),
                                   (1, 512, 2, 128), (1, 512, 4, 128)])
