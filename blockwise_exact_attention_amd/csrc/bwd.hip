@@ -603,6 +603,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
     kt_begin = (int)(jlo / BN);
     kt_end = (int)(jhi / BN) + 1;
   }
+  const float s_mask = p.c > 0.f ? kNegInf : -kNegInf;
   auto step = [&](int kt, const unsigned char* kl, const unsigned char* vl, unsigned char* kn,
                   unsigned char* vn) {
     if (kt + KSPLIT < kt_end) load(kt + KSPLIT, kn, vn);
@@ -624,6 +625,20 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
           const u32x4_t a2 = *reinterpret_cast<const u32x4_t*>(vl + kb * 32 * RB + (ka ^ (32u * s)));
           dpa[kb] = mfma32x32x16(a2, dof[s], s == 0 ? f32x16_t{} : dpa[kb]);
         }
+      // masked scores become -inf * sign(c) (c is never 0), so that P = 0;
+      // masking the scores rather than P keeps the exponentials unconditional
+      // (masking P made the compiler put every exponential under a branch)
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int rel = j - qi;
+            const bool ok = (rel >= p.dlo) & (rel <= p.dhi) & (j < p.l_k);
+            sa[kb][r] = ok ? sa[kb][r] : s_mask;
+          }
+      }
       u32x4_t dsp[NPS];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -632,13 +647,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
           float ds2[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            float pe = __builtin_amdgcn_exp2f(fmaf(sa[kb][r + e], p.c, -l2));
-            if (!full) {
-              const int j = j0 + 32 * kb + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
-              const int rel = j - qi;
-              const bool ok = (rel >= p.dlo) & (rel <= p.dhi) & (j < p.l_k);
-              pe = ok ? pe : 0.f;
-            }
+            const float pe = __builtin_amdgcn_exp2f(fmaf(sa[kb][r + e], p.c, -l2));
             ds2[e] = pe * (dpa[kb][r + e] - dval);
           }
           dsp[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
