@@ -279,26 +279,34 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
             }
         } else if (!full) {
           // Score (kb, r) is key j0 + 4 half + c, c = 32 kb + 8 (r / 4) + r % 4.
-          // This lane's allowed c form one interval lo .. lo + range (from
-          // dlo <= j - qi <= dhi and j < l_k, clamped to the tile; an empty
-          // one gets lo past the tile), so one unsigned compare per score
-          // decides it: half the VALU work of testing the bounds one by one,
-          // which matters where masked tiles are common (the sliding window
-          // at d = 64).  At d = 128 the per-bound form is kept: with it the
-          // compiler schedules the whole step better (measured).
+          // This lane's allowed c form one interval lo64 .. hi64 (from
+          // dlo <= j - qi <= dhi and j < l_k, clamped to the tile), turned
+          // into a 64-bit mask once per tile; each score then costs one
+          // sign-extending bit extract and one bit select, a third of the
+          // VALU work of testing the bounds one by one, which matters where
+          // masked tiles are common (the sliding window at d = 64).  At
+          // d = 128 the per-bound form is kept: with it the compiler
+          // schedules the whole step better (measured: the mask form costs
+          // C2 and C5 ~10%).
           const long long base = (long long)qi - j0 - 4 * half;
           const long long lo64 = max(base + p.dlo, 0LL);
           const long long hi64 = min(min(base + p.dhi, (long long)p.l_k - 1 - j0 - 4 * half),
                                      (long long)BN - 1);
           const bool none = hi64 < lo64;
-          const uint32_t lo = none ? (uint32_t)BN : (uint32_t)lo64;
-          const uint32_t range = none ? 0u : (uint32_t)(hi64 - lo64);
+          // (no compare-to-VCC chain, which costs a wait state per score)
+          const int lo_c = (int)min(lo64, 63LL);  // shift counts kept in range
+          const int hi_c = (int)max(hi64, -1LL);
+          const uint64_t upto = hi_c >= 63 ? ~0ULL : ((1ULL << (hi_c + 1)) - 1);
+          const uint64_t mask = none ? 0ULL : upto & (~0ULL << lo_c);
+          const uint32_t mw[2] = {(uint32_t)mask, (uint32_t)(mask >> 32)};
   #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
   #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const uint32_t c = (uint32_t)(32 * kb + 8 * (r >> 2) + (r & 3));
-              sacc[kb][r] = (c - lo) <= range ? sacc[kb][r] : kNegInf;
+              const int c = 8 * (r >> 2) + (r & 3);  // bit within mw[kb]
+              const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)mw[kb], c, 1);
+              sacc[kb][r] = __uint_as_float((__float_as_uint(sacc[kb][r]) & keep) |
+                                            (0xff800000u & ~keep));
             }
         }
         float mx = kNegInf;
