@@ -9,6 +9,7 @@ kpos <= qpos, inclusive window (win_l, win_r) with -1 for an open side.
 """
 from __future__ import annotations
 
+import contextlib
 import math
 
 import torch
@@ -23,6 +24,13 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
+
+
+def _on(stream):
+    """Context under which buffers for work launched on `stream` are
+    allocated: the caching allocator then ties them to that stream, so a block
+    freed after the call is reused only by work ordered after it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 def _dtype_code(t):
@@ -69,8 +77,9 @@ def attention_forward(q, k, v, scale=None, causal=False, window=(-1, -1),
     n, l_q, h, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out = torch.empty_like(q)
-    lse = torch.empty((n, h, l_q), dtype=torch.float32, device=q.device)
+    with _on(stream):
+        out = torch.empty_like(q)
+        lse = torch.empty((n, h, l_q), dtype=torch.float32, device=q.device)
     return attn_fwd(q, k, v, out, lse, scale, causal, window[0], window[1],
                     q_offset, k_offset, stream)
 
@@ -147,18 +156,52 @@ def bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d):
     return int(_lib.lib().attn_bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d))
 
 
+def _check_bwd(dout, q, k, v, out, lse, dq, dk, dv, acc):
+    """Shapes and dtypes of the backward's tensors against q and k: the C
+    ABI receives bare pointers, so a short tensor here would be read or
+    written past its end.  acc: the gradients are float32 accumulators.
+    Metadata first, then the device: every mismatch raises before anything
+    reaches the library."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [n, l_q, h, d] and k [n, l_k, h_kv, d]")
+    n, l_q, h, d = q.shape
+    if k.shape[0] != n or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [n, l_k, h_kv, d] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    for name, t in (("dout", dout), ("out", out)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    if tuple(lse.shape) != (n, h, l_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [n, h, l_q]")
+    gdt = torch.float32 if acc else q.dtype
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t.shape != ref.shape or t.dtype != gdt:
+            what = "float32 accumulators" if acc else "gradients in q's dtype"
+            raise ValueError(f"{name} must be shaped like {'q' if ref is q else 'k'} "
+                             f"({what})")
+    _dev(dout, q, k, v, out, lse, dq, dk, dv)
+
+
+def _workspace(workspace, need, device, stream):
+    if workspace is None:
+        with _on(stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _dev(workspace)
+    return workspace
+
+
 def attn_bwd(dout, q, k, v, out, lse, dq, dk, dv, scale, causal=False,
              win_l=-1, win_r=-1, q_offset=0, k_offset=0, workspace=None,
              stream=None):
     """Backward into caller-provided dq, dk, dv; `workspace` is a uint8 device
-    tensor of at least bwd_workspace_bytes(...) bytes (allocated if None)."""
-    _dev(dout, q, k, v, out, lse, dq, dk, dv)
+    tensor of at least bwd_workspace_bytes(...) bytes (allocated on `stream`
+    if None)."""
+    _check_bwd(dout, q, k, v, out, lse, dq, dk, dv, acc=False)
     n, l_q, h, d = q.shape
     _, l_k, h_kv, _ = k.shape
     need = bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _dev(workspace)
+    workspace = _workspace(workspace, need, q.device, stream)
     st = _lib.lib().attn_bwd(dout.data_ptr(), q.data_ptr(), k.data_ptr(),
                              v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), n,
@@ -177,16 +220,11 @@ def attn_bwd_acc(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, scale,
     """One ring backward step: this chunk's gradients added to the float32
     accumulators dq_acc (shaped like q), dk_acc and dv_acc (shaped like k);
     out and lse are the query rows' results over the whole sequence."""
-    _dev(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc)
+    _check_bwd(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, acc=True)
     n, l_q, h, d = q.shape
     _, l_k, h_kv, _ = k.shape
-    for a, ref in ((dq_acc, q), (dk_acc, k), (dv_acc, k)):
-        if a.shape != ref.shape or a.dtype != torch.float32:
-            raise ValueError("accumulators must be float32 shaped like q / k")
     need = bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _dev(workspace)
+    workspace = _workspace(workspace, need, q.device, stream)
     st = _lib.lib().attn_bwd_acc(dout.data_ptr(), q.data_ptr(), k.data_ptr(),
                                  v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                  dq_acc.data_ptr(), dk_acc.data_ptr(),
@@ -204,9 +242,10 @@ def attention_backward(dout, q, k, v, out, lse, scale=None, causal=False,
                        window=(-1, -1), q_offset=0, k_offset=0, stream=None):
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    with _on(stream):
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
     return attn_bwd(dout, q, k, v, out, lse, dq, dk, dv, scale, causal,
                     window[0], window[1], q_offset, k_offset, None, stream)
 

@@ -159,13 +159,16 @@ int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
   if (overlap(ra, rq) || overlap(ra, rk) || overlap(ra, rv) ||
       overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ra))
     return ATTN_ERR_ALIAS;
-  // no query rows, or an empty chunk (its rows are all empty and merge as
-  // no-ops): the accumulator stays as it is
-  if (qb == 0 || kb == 0) return ATTN_OK;
+  if (qb == 0) return ATTN_OK;  // no query rows: nothing to merge
+  (void)hipGetLastError();
+  // an empty chunk: every block row is (0, -inf), so rows with a result keep
+  // it and rows still at -inf become O = 0
+  if (kb == 0)
+    return finish(bea::launch_acc_clear_empty(out_acc, lse_acc, n, l_q, h, d,
+                                              static_cast<hipStream_t>(stream)));
 
   AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
   mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
-  (void)hipGetLastError();
   return finish(bea::launch_fwd_bf16(q, k, v, nullptr, nullptr, s,
                                      static_cast<hipStream_t>(stream), out_acc,
                                      lse_acc));

@@ -426,7 +426,8 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
       // ---- epilogue: merge (O / l, LSE) into the accumulator rows.  The
       // weights follow the log1p form of the chunk merge, with the same -inf
       // guards as attn_merge: a block row with no allowed key leaves the row
-      // alone, an accumulator row at -inf is replaced (never multiplied, so
+      // alone (or clears it to O = 0 when the accumulator row is at -inf
+      // too), an accumulator row at -inf is replaced (never multiplied, so
       // whatever it holds cannot leak).  The block's rows pass through LDS
       // in fp32, 16 rows per round in this wave's own 8 KB slice of the
       // first K buffer slots, so that every accumulator access is a whole
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
       const float lb = ltot > 0.f ? (muse + __log2f(ltot)) * kLn2 : kNegInf;
       const size_t li = (size_t)head * p.l_q + min(qi, last_row);
       const float la = p.lse_acc[li];
-      int mode = 0;  // 0 keep, 1 replace, 2 weighted sum
+      int mode = la == kNegInf ? 3 : 0;  // 0 keep, 1 replace, 2 weighted sum, 3 clear
       float wa = 0.f, wb = 0.f;
       if (lb != kNegInf) {
         if (la == kNegInf) {
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
           if (i <= last_row && rmode != 0) {
             f32x4_t* dst = reinterpret_cast<f32x4_t*>(
                 p.acc + ((size_t)b * p.l_q + i) * q_row + (size_t)hq * D + 4 * c);
-            *dst = rmode == 1 ? x : *dst * rwa + x;
+            *dst = rmode == 1 ? x : rmode == 3 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : *dst * rwa + x;
           }
         }
       }

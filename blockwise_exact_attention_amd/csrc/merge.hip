@@ -22,8 +22,10 @@ constexpr int kMergeElems = 2048;  // elements per block on the vector path
 constexpr int kMergeVec = kMergeElems / (4 * kMergeThreads);  // float4 per thread
 
 // Row weights: mode 0 keep the accumulator, 1 take the block, 2 weighted
-// sum.  Computed once per row by one thread and shared through LDS; that
-// thread also writes the row's new LSE (no other thread reads it).
+// sum, 3 clear the row (both sides empty: the merged row is the empty
+// result O = 0, LSE = -inf, whatever the accumulator held).  Computed once
+// per row by one thread and shared through LDS; that thread also writes the
+// row's new LSE (no other thread reads it).
 __device__ __forceinline__ void merge_row_weights(float* __restrict__ lse_acc,
                                                   const float* __restrict__ lse_blk,
                                                   int l, int h, long long row,
@@ -39,7 +41,7 @@ __device__ __forceinline__ void merge_row_weights(float* __restrict__ lse_acc,
   wa = 0.f;
   wb = 0.f;
   if (bb == kNegInf) {
-    mode = 0;
+    mode = a == kNegInf ? 3 : 0;
   } else if (a == kNegInf) {
     mode = 1;
     lse_acc[li] = bb;
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
     int mode = 2;
     float wa = 0.f, wb = 0.f;
     if (bb == kNegInf) {
-      mode = 0;
+      mode = a == kNegInf ? 3 : 0;
     } else if (a == kNegInf) {
       mode = 1;
       lse_acc[li] = bb;
@@ -132,10 +134,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
     if (rr >= nr) continue;
     const int mode = s_mode[rr];
     const size_t off = base + (size_t)rr * row_stride + (e - rr * d);
-    // a row whose accumulator LSE is -inf takes the block as is (select,
-    // never a multiply, so whatever the accumulator held cannot leak)
+    // a row whose accumulator LSE is -inf takes the block as is, or zeros
+    // when the block row is empty too (select, never a multiply, so
+    // whatever the accumulator held cannot leak)
     if (mode == 1)
       *reinterpret_cast<f32x4_t*>(acc + off) = bv[v];
+    else if (mode == 3)
+      *reinterpret_cast<f32x4_t*>(acc + off) = f32x4_t{0.f, 0.f, 0.f, 0.f};
     else if (mode == 2)
       *reinterpret_cast<f32x4_t*>(acc + off) = av[v] * s_wa[rr] + bv[v] * s_wb[rr];
   }
@@ -170,11 +175,41 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const int rr = e / d;
     const int mode = s_mode[rr];
     if (mode == 0) continue;
+    if (mode == 3) {
+      acc[e0 + e] = 0.f;
+      continue;
+    }
     const float bv = BLK_BF16
         ? bf16_lo(static_cast<const uint16_t*>(blk)[e0 + e])
         : static_cast<const float*>(blk)[e0 + e];
     acc[e0 + e] = (mode == 1) ? bv : acc[e0 + e] * s_wa[rr] + bv * s_wb[rr];
   }
+}
+
+// Merge of an empty block (every row's LSE -inf, e.g. a chunk with no keys)
+// into the accumulator: rows at -inf are cleared to O = 0, all others stay.
+// One block per 256 rows; row r of [n, l, h] order (b, i, hq).
+__global__ __launch_bounds__(256) void acc_clear_empty_kernel(float* __restrict__ acc,
+                                                              const float* __restrict__ lse_acc,
+                                                              int l, int h, int d,
+                                                              long long rows) {
+  __shared__ int s_clear[256];
+  const long long r0 = (long long)blockIdx.x * 256;
+  const int nr = (int)min(256LL, rows - r0);
+  const int tid = threadIdx.x;
+  if (tid < nr) {
+    const long long row = r0 + tid;
+    const long long bi = row / h;
+    const int hq = (int)(row - bi * h);
+    const long long b = bi / l;
+    const int i = (int)(bi - b * l);
+    s_clear[tid] = lse_acc[((size_t)b * h + hq) * l + i] == kNegInf;
+  }
+  __syncthreads();
+  const size_t e0 = (size_t)r0 * d;
+  const int ne = nr * d;
+  for (int e = tid; e < ne; e += 256)
+    if (s_clear[e / d]) acc[e0 + e] = 0.f;
 }
 
 // 16-byte stores where the accumulator is 16-byte aligned (n4 = n_acc / 4),
@@ -258,6 +293,14 @@ hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
   else
     hipLaunchKernelGGL((merge_kernel<false>), grid, block, 0, stream, out_acc,
                        lse_acc, out_blk, lse_blk, l, h, d, rows, rpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_acc_clear_empty(float* out_acc, const float* lse_acc, int n, int l,
+                                  int h, int d, hipStream_t stream) {
+  const long long rows = (long long)n * l * h;
+  hipLaunchKernelGGL(acc_clear_empty_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256),
+                     0, stream, out_acc, lse_acc, l, h, d, rows);
   return hipGetLastError();
 }
 

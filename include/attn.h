@@ -46,8 +46,9 @@
  *     h, h_kv and d may not.  A pointer may be NULL exactly when its tensor
  *     has no elements.  With no query rows a call writes nothing; with no
  *     keys (l_k = 0) every row is empty: attn_fwd writes O = 0 and
- *     LSE = -inf, attn_fwd_acc leaves the accumulator as it is (an empty
- *     chunk merges as a no-op), attn_bwd writes dQ = 0 (and dK = dV = 0 when
+ *     LSE = -inf, attn_fwd_acc merges the empty block like attn_merge does
+ *     (rows with a result keep it, rows at LSE -inf get O = 0), attn_bwd
+ *     writes dQ = 0 (and dK = dV = 0 when
  *     l_q = 0 instead), attn_bwd_acc adds nothing.  These are the pages'
  *     fully-masked conventions applied to a chunk with no rows or no keys.
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Every
@@ -113,10 +114,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  * update_out_and_lse, sigmoid form - the two are equal):
  *   lse = max(a,b) + log1p(exp(min(a,b) - max(a,b)))
  *   out_acc = out_acc * exp(a - lse) + float(out_blk) * exp(b - lse)
- * with a = lse_acc, b = lse_blk per row (b, hq, i).  If b = -inf the row is
- * left unchanged; if a = -inf (and b is not) the row becomes (out_blk, b)
- * whatever out_acc held before, so an uninitialised accumulator with LSE
- * -inf is safe.
+ * with a = lse_acc, b = lse_blk per row (b, hq, i).  If b = -inf and a is
+ * finite the row is left unchanged; if a = -inf and b is finite the row
+ * becomes (out_blk, b); if both are -inf the row becomes the empty result
+ * (O = 0, LSE = -inf).  A row at a = -inf is written without reading
+ * out_acc, so an accumulator whose O holds anything (NaN included) is safe
+ * wherever its LSE is -inf.
  *
  *   out_acc [n,l,h,d] float32  in/out      lse_acc [n,h,l] float32 in/out
  *   out_blk [n,l,h,d] blk_dtype in         lse_blk [n,h,l] float32 in
@@ -133,8 +136,9 @@ int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
  * followed by the merge).  The result equals attn_fwd into a block (O, LSE)
  * followed by attn_merge of that block, except that the block's O is merged
  * in float32 instead of being rounded to the query dtype first; the same
- * -inf guards apply (a row with no allowed key in this chunk is left alone;
- * an accumulator row at -inf is replaced, whatever it held).
+ * -inf guards apply (a row with no allowed key in this chunk is left alone,
+ * or set to O = 0 when the accumulator row is at -inf too; an accumulator
+ * row at -inf is replaced, whatever it held).
  *
  *   q       [n,l_q,h,d]     in      bfloat16 (dtype must be ATTN_BF16)
  *   k,v     [n,l_k,h_kv,d]  in      bfloat16

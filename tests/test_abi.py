@@ -120,7 +120,9 @@ def test_empty_inputs_need_no_pointers_and_launch_nothing():
     """Zero rows (n = 0 or l_q = 0), or an empty chunk for the calls that then
     leave their outputs alone, return ATTN_OK before any HIP call, with NULL
     for every tensor that has no elements.  A NULL pointer to a non-empty
-    tensor is still an error."""
+    tensor is still an error.  (A fused ring step over an empty chunk does
+    launch: accumulator rows still at -inf are cleared to O = 0; the GPU
+    tests cover it.)"""
     L = _lib.lib()
     nul = dict(q=None, k=None, v=None, out=None, lse=None)
     assert _fwd(n=0, **nul) == ATTN_OK
@@ -129,7 +131,6 @@ def test_empty_inputs_need_no_pointers_and_launch_nothing():
     assert _fwd(l_k=0, k=None, v=None, out=None) == ATTN_ERR_NULL   # O has rows
     assert _fwd(n=0, h=0, **nul) == ATTN_ERR_SHAPE
     assert _fwd_acc(l_q=0, q=None, acc=None, lse=None) == ATTN_OK
-    assert _fwd_acc(l_k=0, k=None, v=None) == ATTN_OK   # empty chunk: no-op
     assert _fwd_acc(l_k=0, k=None, v=None, acc=None) == ATTN_ERR_NULL
     assert L.attn_merge(None, None, None, None, 1, 0, 2, 64, ATTN_BF16, None) == ATTN_OK
     assert L.attn_merge(None, None, None, None, 0, 5, 2, 64, ATTN_BF16, None) == ATTN_OK
@@ -286,3 +287,62 @@ def test_host_tensors_are_rejected():
         A.attn_fwd(q, q, q, q.clone(), lse, 0.125)
     with pytest.raises(ValueError, match="GPU"):
         A.attn_merge(lse.new_zeros((1, 8, 2, 64)), lse.clone(), q, lse)
+
+
+def _bwd_set(acc=False):
+    """Consistent host tensors for the backward wrappers: q-shaped dout, q,
+    out, dq and k-shaped k, v, dk, dv (GQA 4/2), LSE [n, h, l_q]."""
+    import torch
+    bf = torch.bfloat16
+    gd = torch.float32 if acc else bf
+    n, l_q, l_k, h, h_kv, d = 1, 8, 12, 4, 2, 64
+    t = dict(dout=torch.zeros((n, l_q, h, d), dtype=bf),
+             q=torch.zeros((n, l_q, h, d), dtype=bf),
+             k=torch.zeros((n, l_k, h_kv, d), dtype=bf),
+             v=torch.zeros((n, l_k, h_kv, d), dtype=bf),
+             out=torch.zeros((n, l_q, h, d), dtype=bf),
+             lse=torch.zeros((n, h, l_q)),
+             dq=torch.zeros((n, l_q, h, d), dtype=gd),
+             dk=torch.zeros((n, l_k, h_kv, d), dtype=gd),
+             dv=torch.zeros((n, l_k, h_kv, d), dtype=gd))
+    return t
+
+
+@pytest.mark.parametrize("acc", [False, True])
+@pytest.mark.parametrize("field,bad", [
+    ("dout", "short"), ("out", "short"), ("out", "dtype"), ("v", "short"),
+    ("v", "dtype"), ("lse", "short"), ("lse", "dtype"), ("dq", "short"),
+    ("dq", "dtype"), ("dk", "short"), ("dv", "short"), ("dv", "dtype"),
+    ("k", "head_dim")])
+def test_bwd_wrapper_rejects_mismatched_tensors(acc, field, bad):
+    """The backward wrappers check all nine tensors against q and k before
+    anything reaches the library (which receives bare pointers and could not
+    tell a short tensor): each mismatch raises ValueError naming the shape
+    problem, not the device."""
+    import torch
+    from blockwise_exact_attention_amd import attention as A
+    t = _bwd_set(acc)
+    x = t[field]
+    if bad == "short":
+        t[field] = x[..., :-1].contiguous() if field == "lse" else x[:, :-1].contiguous()
+    elif bad == "dtype":
+        t[field] = x.to(torch.float16 if x.dtype == torch.float32 else torch.float32)
+    else:
+        t["k"] = x[..., :32].contiguous()
+    fn = A.attn_bwd_acc if acc else A.attn_bwd
+    with pytest.raises(ValueError) as e:
+        fn(t["dout"], t["q"], t["k"], t["v"], t["out"], t["lse"], t["dq"], t["dk"],
+           t["dv"], 0.125, True)
+    assert "GPU" not in str(e.value)
+
+
+@pytest.mark.parametrize("acc", [False, True])
+def test_bwd_wrapper_consistent_host_tensors_reach_the_device_check(acc):
+    """A consistent set passes every shape check and is then refused only
+    because it is on the host."""
+    from blockwise_exact_attention_amd import attention as A
+    t = _bwd_set(acc)
+    fn = A.attn_bwd_acc if acc else A.attn_bwd
+    with pytest.raises(ValueError, match="GPU"):
+        fn(t["dout"], t["q"], t["k"], t["v"], t["out"], t["lse"], t["dq"], t["dk"],
+           t["dv"], 0.125, True)

@@ -1,8 +1,10 @@
 """Empty inputs through the C ABI on the GPU: no keys (every row empty: O = 0,
-LSE = -inf, dQ = 0; a fused ring step or accumulating backward step leaves
-its accumulators alone), no query rows (dK = dV = 0), zero batch, and a ring
-share with an empty chunk among its chunks.  Expected values are the oracle's
-(fully-masked rows) or the untouched inputs."""
+LSE = -inf, dQ = 0; a fused ring step or a merge of the empty block keeps
+the accumulator rows that hold a result and clears those at -inf to O = 0;
+an accumulating backward step leaves its accumulators alone), no query rows
+(dK = dV = 0), zero batch, and a ring share with an empty chunk among its
+chunks.  Expected values are the oracle's (fully-masked rows, its merge) or
+the untouched inputs."""
 import numpy as np
 import pytest
 import torch
@@ -44,15 +46,26 @@ def test_forward_without_rows_or_batch():
         assert o.numel() == 0 and lse.numel() == 0
 
 
-def test_fused_step_and_merge_leave_accumulator_for_empty_chunk():
+def test_fused_step_and_merge_of_an_empty_chunk():
     (q, acc, lacc) = rand(602, [(1, 50, 4, 128), (1, 50, 4, 128), (1, 4, 50)], "f32")
     q = round_to_bf16(q)
     tq = dev(q, "bf16")
     tk = torch.zeros((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    # a fifth of the accumulator rows empty, holding garbage
+    empty = np.random.default_rng(602).random((1, 4, 50)) < 0.2
+    assert empty.any() and not empty.all()
+    lacc = lacc.copy()
+    lacc[empty] = -np.inf
+    ref_o, ref_l = oracle.merge(acc, lacc, np.zeros_like(acc),
+                                np.full_like(lacc, -np.inf))
+    acc = acc.copy()
+    acc[np.transpose(empty, (0, 2, 1))] = np.nan
     tacc = torch.from_numpy(acc).cuda()
     tl = torch.from_numpy(lacc).cuda()
-    a0, l0 = tacc.clone(), tl.clone()
     A.attn_fwd_acc(tq, tk, tk, tacc, tl, 0.1, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(tacc), ref_o) and np.array_equal(host(tl), ref_l)
+    a0, l0 = tacc.clone(), tl.clone()
     # the unfused ring step: forward of the empty chunk, then the merge
     blk, lblk = A.attention_forward(tq, tk, tk, 0.1, True)
     A.attn_merge(tacc, tl, blk, lblk)

@@ -59,8 +59,7 @@ def test_c2_causal_mha_full():
 
 def test_c3_ring_share():
     """Rank 7 of 8: the merged share equals rows 7168..8191 of causal
-    attention over the full 8192-token sequence (sampled heads, one from
-    each key/value group and both ends of a group)."""
+    attention over the full 8192-token sequence, on every head and row."""
     w = WORKLOADS["C3"]
     say(f"[C3] {w}")
     x = make_inputs(w)
@@ -68,11 +67,11 @@ def test_c3_ring_share():
     kc = [dev(c, "bf16") for c in x["k_chunks"]]
     vc = [dev(c, "bf16") for c in x["v_chunks"]]
     share = A.RingShare(tq, w.softmax_scale, True, x["q_offset"])
-    heads = [(0, 0), (0, 3), (0, 6), (0, 13), (0, 21), (0, 31)]
+    heads = None  # all 32
     q_full_rows = x["q"]
     ro, rl = oracle.attention_fwd(q_full_rows, x["k_full"], x["v_full"],
                                   w.softmax_scale, True, -1, -1,
-                                  x["q_offset"], 0, heads=heads)
+                                  x["q_offset"], 0, heads=heads, block=1024)
     for fused in (False, True):
         out, lse_acc = share.run(kc, vc, x["k_offsets"], fused=fused)
         torch.cuda.synchronize()
@@ -106,19 +105,17 @@ def test_c4_sliding_window_full():
     check_o_lse(o, lse, ro, rl, "bf16", "C4")
 
 
-def test_c5_forward_sampled_rows():
+def test_c5_forward_full():
+    """The 16384-token causal workload at full size, every head and row (the
+    oracle goes head by head, about two seconds each on a 16-thread host)."""
     w = WORKLOADS["C5"]
     say(f"[C5 fwd] {w}")
     x = make_inputs(w)
     o, lse = run_fwd(x["q"], x["k"], x["v"], "bf16", w.softmax_scale, True)
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([
-        [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, 8191, 8192, 16383],
-        rng.integers(0, w.l_q, 200)]))
-    heads = [(0, 0), (0, 7), (0, 15)]
-    ro, rl = oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale,
-                                  True, heads=heads, rows=rows)
-    check_o_lse(o, lse, ro, rl, "bf16", "C5 forward (sampled rows)")
+    for hq in range(w.h):
+        ro, rl = oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale,
+                                      True, heads=[(0, hq)], block=1024)
+        check_o_lse(o, lse, ro, rl, "bf16", f"C5 forward head {hq}")
 
 
 # ---------------------------------------------------------------- small cases
@@ -233,12 +230,15 @@ def test_merge_parity(d, blk_dtype):
     torch.cuda.synchronize()
     ro, rl = oracle.merge(oa, la, ob, lb)
     go, gl = host(acc), host(lacc)
-    both = np.transpose(np.isneginf(la) & np.isneginf(lb), (0, 2, 1))
-    keep = ~np.broadcast_to(both[..., None], go.shape)
+    # every row, the both-empty ones included (there the merge gives O = 0,
+    # whatever the accumulator held: NaN above)
+    both = np.isneginf(la) & np.isneginf(lb)
+    assert both.any()
     assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
     fin = np.isfinite(rl)
     assert np.max(np.abs(gl[fin] - rl[fin])) < 2e-6
-    assert np.max(np.abs(go[keep] - ro[keep])) < 2e-5
+    assert np.all(np.isfinite(go))
+    assert np.max(np.abs(go - ro)) < 2e-5
 
 
 def test_acc_init_and_cast():

@@ -47,20 +47,21 @@ def test_random_forward_and_fused_step(seed):
     torch.cuda.synchronize()
     ro, rl = oracle.attention_fwd(q, k, v, scale, causal, wl, wr, qo, ko)
     check_o_lse(host(o), host(lse), ro, rl, "bf16", f"seed {seed}")
-    # the fused ring step on a random accumulator (a third of its rows empty)
+    # the fused ring step on a random accumulator (a third of its rows empty,
+    # holding garbage: an empty accumulator row's O must not leak, and where
+    # this chunk gives the row no key either the merge gives O = 0)
     rng = np.random.default_rng(seed + 1)
     acc0 = rng.standard_normal((n, l_q, h, d)).astype(np.float32)
     lse0 = (rng.standard_normal((n, h, l_q)) * 2).astype(np.float32)
-    lse0[rng.random((n, h, l_q)) < 0.33] = -np.inf
-    acc = torch.from_numpy(acc0).cuda()
+    empty0 = rng.random((n, h, l_q)) < 0.33
+    lse0[empty0] = -np.inf
+    acc_in = acc0.copy()
+    acc_in[np.transpose(empty0, (0, 2, 1))] = 1e30
+    acc = torch.from_numpy(acc_in).cuda()
     lacc = torch.from_numpy(lse0).cuda()
     A.attn_fwd_acc(tq, tk, tv, acc, lacc, scale, causal, wl, wr, qo, ko)
     torch.cuda.synchronize()
     mo, ml = oracle.merge(acc0, lse0, ro, rl)
-    # a row this chunk gives no key is left as it was (also when the
-    # accumulator row is empty too, where the merge itself returns O = 0)
-    keep = np.transpose(np.isneginf(rl), (0, 2, 1))
-    mo[keep] = acc0[keep]
     check_o_lse(host(acc), host(lacc), mo, ml, "bf16", f"seed {seed} fused")
 
 

@@ -81,3 +81,29 @@ def test_two_host_threads_two_streams():
         t.join(timeout=120)
     assert not any(t.is_alive() for t in ts), "a worker thread did not finish"
     assert not errors, errors
+
+
+def test_backward_on_a_side_stream_while_another_is_current():
+    """stream= names a stream other than the current one: the wrapper's
+    workspace and outputs belong to that stream, so memory the current
+    stream allocates and fills right after the call (before any
+    synchronisation) cannot be the workspace the backward is still reading."""
+    say("[streams] backward with stream= a side stream, the default stream current")
+    q, k, v = inputs(705, l=1024, h=8, h_kv=2)
+    do, _, _ = inputs(706, l=1024, h=8, h_kv=2)
+    o, lse = A.attention_forward(q, k, v, 0.1, True)
+    ref = A.attention_backward(do, q, k, v, o, lse, 0.1, True)
+    # 1024 keys of 2 key/value heads give the dK/dV kernel few workgroups,
+    # so the workspace also holds split partials; then the same call on a
+    # side stream
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    for rep in range(3):
+        got = A.attention_backward(do, q, k, v, o, lse, 0.1, True, stream=s)
+        # the current (default) stream grabs memory and overwrites it at once
+        junk = [torch.full((1 << 22,), float(rep + 1), device="cuda") for _ in range(8)]
+        s.synchronize()
+        torch.cuda.synchronize()
+        for g, r in zip(got, ref):
+            assert torch.equal(g, r), f"repetition {rep}: gradients differ"
+        del junk, got

@@ -550,3 +550,111 @@ def test_pins_catch_planted_mistakes():
     ]
     for m in mutants:
         assert not np.allclose(m, bo, atol=1e-6)
+
+
+# ---------------------------------------------------------------- row blocks and sampling
+
+@pytest.mark.parametrize("mask", MASKS)
+def test_brute_force_across_row_blocks(mask):
+    """The oracle's row blocks do not change the result: with block=2 (four
+    or five blocks over 7-9 rows, the last one ragged) the forward still
+    equals the pure-Python brute force, and the backward equals its own
+    one-block result and torch autograd through the dense definition."""
+    causal, wl, wr, qo, ko = mask
+    rng = np.random.default_rng(abs(hash(("blocks", mask))) % 2**32)
+    n, l_q, l_k, h, h_kv, d = 2, 9, 8, 4, 2, 5
+    q = _rand(rng, n, l_q, h, d)
+    k = _rand(rng, n, l_k, h_kv, d)
+    v = _rand(rng, n, l_k, h_kv, d)
+    do = _rand(rng, n, l_q, h, d)
+    o, lse = oracle.attention_fwd(q, k, v, 0.8, causal, wl, wr, qo, ko, block=2)
+    bo, blse = brute_attention(q.tolist(), k.tolist(), v.tolist(), 0.8, causal,
+                               wl, wr, qo, ko)
+    bo, blse = np.array(bo), np.array(blse)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(blse))
+    fin = np.isfinite(blse)
+    np.testing.assert_allclose(lse[fin], blse[fin], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    g2 = oracle.attention_bwd(q, k, v, do, 0.8, causal, wl, wr, qo, ko, block=2)
+    g1 = oracle.attention_bwd(q, k, v, do, 0.8, causal, wl, wr, qo, ko, block=64)
+    for a, b in zip(g2, g1):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    # autograd through the dense masked softmax, independent of the blocks
+    m = oracle.allowed_mask(np.arange(l_q), np.arange(l_k), causal, wl, wr, qo, ko)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    kk = tk.repeat_interleave(h // h_kv, dim=2)
+    vv = tv.repeat_interleave(h // h_kv, dim=2)
+    s = torch.einsum("nihd,njhd->nhij", tq, kk) * 0.8
+    tm = torch.from_numpy(m)
+    rows = tm.any(dim=1)
+    s = s.masked_fill(~tm, float("-inf")).masked_fill(~rows[:, None].expand_as(tm), 0.0)
+    p = torch.softmax(s, dim=-1) * rows[:, None]
+    (torch.einsum("nhij,njhd->nihd", p, vv) * torch.from_numpy(do)).sum().backward()
+    for a, t in zip(g2, (tq, tk, tv)):
+        np.testing.assert_allclose(a, t.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_sampling_arguments_select_without_changing_values():
+    """heads= and rows= (forward) and kv_heads= (backward) compute exactly the
+    entries of the full call and leave every other entry NaN; the GPU checks
+    at full size rely on these samples."""
+    rng = np.random.default_rng(31)
+    n, l_q, l_k, h, h_kv, d = 2, 13, 11, 6, 3, 4
+    q = _rand(rng, n, l_q, h, d)
+    k = _rand(rng, n, l_k, h_kv, d)
+    v = _rand(rng, n, l_k, h_kv, d)
+    do = _rand(rng, n, l_q, h, d)
+    args = (0.6, True, 5, -1, 2, 0)
+    o, lse = oracle.attention_fwd(q, k, v, *args, block=3)
+    heads = [(1, 4), (0, 0), (1, 1)]
+    rows = [12, 0, 5, 6, 7]
+    so, sl = oracle.attention_fwd(q, k, v, *args, heads=heads, rows=rows, block=2)
+    sel_o = np.zeros(o.shape, bool)
+    sel_l = np.zeros(lse.shape, bool)
+    for b, hq in heads:
+        sel_o[b, rows, hq, :] = True
+        sel_l[b, hq, rows] = True
+    assert np.all(np.isnan(so[~sel_o])) and np.all(np.isnan(sl[~sel_l]))
+    # (different row blocks keep different key columns: rounding-level
+    # differences only)
+    np.testing.assert_allclose(so[sel_o], o[sel_o], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sl[sel_l], lse[sel_l], rtol=0, atol=1e-13)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, *args)
+    kvh = [(1, 2), (0, 1)]
+    sq, sk, sv = oracle.attention_bwd(q, k, v, do, *args, kv_heads=kvh, block=4)
+    sel_q = np.zeros(dq.shape, bool)
+    sel_k = np.zeros(dk.shape, bool)
+    for b, g in kvh:
+        sel_q[b, :, 2 * g:2 * g + 2, :] = True   # the group's query heads
+        sel_k[b, :, g, :] = True
+    for full, samp, sel in ((dq, sq, sel_q), (dk, sk, sel_k), (dv, sv, sel_k)):
+        assert np.all(np.isnan(samp[~sel]))
+        np.testing.assert_allclose(samp[sel], full[sel], rtol=0, atol=1e-13)
+
+
+def test_ring_share_head_sample_equals_full_rows():
+    """ring_share(heads=...) merges exactly the sampled heads: their rows equal
+    full-sequence attention; the other heads stay at the empty result."""
+    rng = np.random.default_rng(32)
+    P, c, h, h_kv, d = 4, 5, 6, 2, 3
+    q = _rand(rng, 2, P * c, h, d)
+    k = _rand(rng, 2, P * c, h_kv, d)
+    v = _rand(rng, 2, P * c, h_kv, d)
+    o_full, l_full = oracle.attention_fwd(q, k, v, 0.5, True)
+    heads = [(0, 5), (1, 0), (1, 3)]
+    r = 2
+    kc = [k[:, s * c:(s + 1) * c] for s in range(P)]
+    vc = [v[:, s * c:(s + 1) * c] for s in range(P)]
+    o, lse = oracle.ring_share(q[:, r * c:(r + 1) * c], kc, vc, 0.5, True, r * c,
+                               [s * c for s in range(P)], heads=heads)
+    for b in range(2):
+        for hq in range(h):
+            if (b, hq) in heads:
+                np.testing.assert_allclose(o[b, :, hq], o_full[b, r * c:(r + 1) * c, hq],
+                                           atol=1e-12)
+                np.testing.assert_allclose(lse[b, hq], l_full[b, hq, r * c:(r + 1) * c],
+                                           atol=1e-12)
+            else:
+                assert np.all(o[b, :, hq] == 0.0) and np.all(np.isneginf(lse[b, hq]))
