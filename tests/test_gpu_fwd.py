@@ -346,12 +346,14 @@ def test_fwd_acc_merges_into_accumulator(case):
     ob_m = np.where(np.isnan(ob), 0.0, ob)
     acc0_clean = np.where(np.isnan(acc_in), 0.0, acc_in)
     ro, rl = oracle.merge(acc0_clean, lse0, ob_m, lb_m)
-    # a row with no allowed key in this chunk must be left exactly as it was
-    # (NaN content included); it is checked apart from the merged rows
-    keep = sel & np.isneginf(lb)
-    merged = sel & ~keep
-    ro = np.where(np.transpose(merged, (0, 2, 1))[..., None], ro, np.nan)
-    rl = np.where(merged, rl, np.nan)
+    # every sampled row against the merge (where the accumulator row is
+    # empty its NaN content must not leak: the merge there is the block, or
+    # O = 0 when this chunk gives the row no key either); besides, a row
+    # with a result and no allowed key in this chunk is left bit for bit
+    keep = sel & np.isneginf(lb) & ~empty
+    cleared = sel & np.isneginf(lb) & empty
+    ro = np.where(np.transpose(sel, (0, 2, 1))[..., None], ro, np.nan)
+    rl = np.where(sel, rl, np.nan)
     acc = torch.from_numpy(acc_in).cuda()
     lse_acc = torch.from_numpy(lse0).cuda()
     A.attn_fwd_acc(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), acc, lse_acc,
@@ -361,5 +363,7 @@ def test_fwd_acc_merges_into_accumulator(case):
     check_o_lse(go.astype(np.float64), gl.astype(np.float64), ro, rl, "bf16",
                 str(case))
     kr = np.transpose(keep, (0, 2, 1))
-    assert np.array_equal(go[kr], acc_in[kr], equal_nan=True)
+    assert np.array_equal(go[kr], acc_in[kr])
     assert np.array_equal(gl[keep], lse0[keep])
+    cr = np.transpose(cleared, (0, 2, 1))
+    assert np.all(go[cr] == 0.0) and np.all(np.isneginf(gl[cleared]))
