@@ -20,6 +20,8 @@ ATTN_ERR_ALIGN = 7
 ATTN_F32 = 0
 ATTN_BF16 = 1
 
+ATTN_RING_MAX_CHUNKS = 16
+
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
@@ -31,6 +33,10 @@ SIGNATURES = {
                       _i, _i, _ll, _ll, _vp, _i]),
     "attn_fwd_acc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                           _i, _i, _ll, _ll, _vp, _i]),
+    "attn_fwd_ring": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
+                           _f, _i, _i, _i, _ll, _vp, _i]),
+    "attn_fwd_kernel_name": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _ll,
+                                               _ll, _i, _i]),
     "attn_merge": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_acc_init": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_acc_cast": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp]),

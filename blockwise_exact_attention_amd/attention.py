@@ -10,6 +10,7 @@ kpos <= qpos, inclusive window (win_l, win_r) with -1 for an open side.
 from __future__ import annotations
 
 import contextlib
+import ctypes
 import math
 
 import torch
@@ -71,6 +72,20 @@ def attn_fwd(q, k, v, out, lse, scale, causal=False, win_l=-1, win_r=-1,
     return out, lse
 
 
+def fwd_kernel_name(n, l_q, l_k, h, h_kv, d, causal=False, win_l=-1, win_r=-1,
+                    q_offset=0, k_offset=0, dtype=torch.bfloat16, fused=False,
+                    scale=None):
+    """Name of the kernel attn_fwd (or, fused, attn_fwd_acc) launches for
+    these arguments, as kernel traces show it; None if none would run."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    r = _lib.lib().attn_fwd_kernel_name(n, l_q, l_k, h, h_kv, d, float(scale),
+                                        int(bool(causal)), int(win_l), int(win_r),
+                                        int(q_offset), int(k_offset), _DT[dtype],
+                                        int(bool(fused)))
+    return None if r is None else r.decode()
+
+
 def attention_forward(q, k, v, scale=None, causal=False, window=(-1, -1),
                       q_offset=0, k_offset=0, stream=None):
     """Allocate (O, LSE) and run the forward; scale defaults to 1/sqrt(d)."""
@@ -124,6 +139,42 @@ def attn_fwd_acc(q, k, v, out_acc, lse_acc, scale, causal=False, win_l=-1,
                                  _dtype_code(q))
     check("attn_fwd_acc", st)
     return out_acc, lse_acc
+
+
+def attn_fwd_ring(q, k_chunks, v_chunks, k_offsets, out, lse, scale, causal=False,
+                  win_l=-1, win_r=-1, q_offset=0, stream=None):
+    """A whole ring share in one launch: bf16 q against every k/v chunk (key j
+    of chunk c at absolute position k_offsets[c] + j), written to `out` (bf16,
+    like q) and `lse` (float32 [n, h, l_q])."""
+    nc = len(k_chunks)
+    if len(v_chunks) != nc or len(k_offsets) != nc:
+        raise ValueError("k_chunks, v_chunks and k_offsets must have one entry per chunk")
+    if not 1 <= nc <= _lib.ATTN_RING_MAX_CHUNKS:
+        raise ValueError(f"1 to {_lib.ATTN_RING_MAX_CHUNKS} chunks, got {nc}")
+    _dev(q, out, lse, *k_chunks, *v_chunks)
+    n, l_q, h, d = q.shape
+    h_kv = k_chunks[0].shape[2]
+    for kc, vc in zip(k_chunks, v_chunks):
+        if kc.shape != vc.shape or kc.dim() != 4 or kc.shape[0] != n or \
+                kc.shape[2] != h_kv or kc.shape[3] != d:
+            raise ValueError("every k and v chunk must be [n, l_k, h_kv, d] matching q")
+        if kc.dtype != q.dtype or vc.dtype != q.dtype:
+            raise ValueError("q and the chunks must share a dtype")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(lse.shape) != (n, h, l_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [n, h, l_q]")
+    ptrs = ctypes.c_void_p * nc
+    kp = ptrs(*[c.data_ptr() for c in k_chunks])
+    vp = ptrs(*[c.data_ptr() for c in v_chunks])
+    lk = (ctypes.c_int * nc)(*[c.shape[1] for c in k_chunks])
+    ko = (ctypes.c_longlong * nc)(*[int(o) for o in k_offsets])
+    st = _lib.lib().attn_fwd_ring(q.data_ptr(), kp, vp, lk, ko, nc, out.data_ptr(),
+                                  lse.data_ptr(), n, l_q, h, h_kv, d, float(scale),
+                                  int(bool(causal)), int(win_l), int(win_r),
+                                  int(q_offset), _stream(stream), _dtype_code(q))
+    check("attn_fwd_ring", st)
+    return out, lse
 
 
 def attn_acc_init(out_acc, lse_acc=None, stream=None):
@@ -293,7 +344,10 @@ class RingShare:
     final output.  `run` launches acc_init, then per key/value chunk (with
     that chunk's absolute offset) either attn_fwd + attn_merge or, with
     fused=True, the single attn_fwd_acc step, then the final cast - all on
-    one stream, nothing synchronised (flash_sharding.py, ring_fwd)."""
+    one stream, nothing synchronised (flash_sharding.py, ring_fwd).  With
+    one_launch=True (bf16, at most ATTN_RING_MAX_CHUNKS chunks) the whole
+    share is the single attn_fwd_ring launch instead, writing the final O and
+    LSE directly."""
 
     def __init__(self, q, scale, causal, q_offset, window=(-1, -1)):
         n, l, h, d = q.shape
@@ -309,7 +363,14 @@ class RingShare:
         self.lse_blk = torch.empty((n, h, l), dtype=torch.float32, device=dev)
         self.out = torch.empty_like(q)
 
-    def run(self, k_chunks, v_chunks, k_offsets, stream=None, fused=False):
+    def run(self, k_chunks, v_chunks, k_offsets, stream=None, fused=False,
+            one_launch=False):
+        if one_launch:
+            wl, wr = self.window
+            # lse_acc holds the share's final LSE, as after the other forms
+            attn_fwd_ring(self.q, k_chunks, v_chunks, k_offsets, self.out, self.lse_acc,
+                          self.scale, self.causal, wl, wr, self.q_offset, stream)
+            return self.out, self.lse_acc
         attn_acc_init(self.acc, self.lse_acc, stream)
         for kc, vc, ko in zip(k_chunks, v_chunks, k_offsets):
             wl, wr = self.window
@@ -345,11 +406,12 @@ def _capture(fn):
 
 
 def ring_share(q, k_chunks, v_chunks, k_offsets, q_offset, scale=None,
-               causal=True, stream=None, fused=False, window=(-1, -1)):
+               causal=True, stream=None, fused=False, window=(-1, -1),
+               one_launch=False):
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     return RingShare(q, scale, causal, q_offset, window).run(
-        k_chunks, v_chunks, k_offsets, stream, fused)
+        k_chunks, v_chunks, k_offsets, stream, fused, one_launch)
 
 
 class RingShareBwd:

@@ -11,6 +11,7 @@
 namespace {
 
 using bea::AttnShape;
+static_assert(ATTN_RING_MAX_CHUNKS == bea::kMaxChunks, "chunk limit of the one-launch share");
 
 // a, b: counts that may be zero (batch, sequence length); c, d: layout
 // sizes that must be positive (heads, head dim).
@@ -133,8 +134,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                                        (int)(d * es / 4), hs));
   AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
   mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
-  return finish(dtype == ATTN_BF16 ? bea::launch_fwd_bf16(q, k, v, out, lse, s, hs)
-                                   : bea::launch_fwd_f32(q, k, v, out, lse, s, hs));
+  if (dtype == ATTN_F32) return finish(bea::launch_fwd_f32(q, k, v, out, lse, s, hs));
+  const bea::FwdChunk ch{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), l_k,
+                         s.dlo, s.dhi};
+  if (bea::fwd_pipe_preferred(&ch, 1, s))
+    return finish(bea::launch_fwd_pipe(q, &ch, 1, out, lse, s, hs));
+  return finish(bea::launch_fwd_bf16(q, k, v, out, lse, s, hs));
 }
 
 int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
@@ -169,9 +174,77 @@ int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
 
   AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
   mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
-  return finish(bea::launch_fwd_bf16(q, k, v, nullptr, nullptr, s,
-                                     static_cast<hipStream_t>(stream), out_acc,
-                                     lse_acc));
+  const bea::FwdChunk ch{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), l_k,
+                         s.dlo, s.dhi};
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (bea::fwd_pipe_preferred(&ch, 1, s))
+    return finish(bea::launch_fwd_pipe(q, &ch, 1, nullptr, nullptr, s, hs, out_acc, lse_acc));
+  return finish(bea::launch_fwd_bf16(q, k, v, nullptr, nullptr, s, hs, out_acc, lse_acc));
+}
+
+const char* attn_fwd_kernel_name(int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
+                                 int causal, int win_l, int win_r, long long q_offset,
+                                 long long k_offset, int dtype, int fused) {
+  if (check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype) != ATTN_OK) return nullptr;
+  if (fused && dtype != ATTN_BF16) return nullptr;
+  if ((long long)n * l_q == 0 || l_k == 0) return nullptr;  // no attention kernel runs
+  AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+  mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
+  if (dtype == ATTN_F32) return d == 128 ? "fwd_f32_kernel<128>" : "fwd_f32_kernel<64>";
+  const bea::FwdChunk ch{nullptr, nullptr, l_k, s.dlo, s.dhi};
+  if (bea::fwd_pipe_preferred(&ch, 1, s)) return bea::fwd_pipe_kernel_name(&ch, 1, s, fused);
+  return bea::fwd_bf16_kernel_name(s, fused);
+}
+
+int attn_fwd_ring(const void* q, const void* const* k_chunks, const void* const* v_chunks,
+                  const int* l_k_chunks, const long long* k_offsets, int n_chunks, void* out,
+                  float* lse, int n, int l_q, int h, int h_kv, int d, float scale, int causal,
+                  int win_l, int win_r, long long q_offset, void* stream, int dtype) {
+  if (n_chunks < 1 || n_chunks > ATTN_RING_MAX_CHUNKS) return ATTN_ERR_SHAPE;
+  if (k_chunks == nullptr || v_chunks == nullptr || l_k_chunks == nullptr ||
+      k_offsets == nullptr)
+    return ATTN_ERR_NULL;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int st = check_attn_args(n, l_q, l_k_chunks[c], h, h_kv, d, scale, dtype);
+    if (st != ATTN_OK) return st;
+  }
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const long long qb = (long long)n * l_q * h * d * 2;
+  const long long lb = (long long)n * h * l_q * 4;
+  if (missing(q, qb) || missing(out, qb) || missing(lse, lb)) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+  const Range rq = range(q, qb), ro = range(out, qb), rl = range(lse, lb);
+  if (overlap(ro, rq) || overlap(rl, rq) || overlap(rl, ro)) return ATTN_ERR_ALIAS;
+  for (int c = 0; c < n_chunks; ++c) {
+    const long long kb = (long long)n * l_k_chunks[c] * h_kv * d * 2;
+    if (missing(k_chunks[c], kb) || missing(v_chunks[c], kb)) return ATTN_ERR_NULL;
+    if (!aligned(k_chunks[c], 16) || !aligned(v_chunks[c], 16)) return ATTN_ERR_ALIGN;
+    const Range rk = range(k_chunks[c], kb), rv = range(v_chunks[c], kb);
+    if (overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rk) || overlap(rl, rv))
+      return ATTN_ERR_ALIAS;
+  }
+  if (qb == 0) return ATTN_OK;  // no query rows: nothing to write
+
+  (void)hipGetLastError();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // chunks without keys add nothing: drop them
+  bea::FwdChunk ch[bea::kMaxChunks];
+  int m = 0;
+  AttnShape s{n, l_q, 0, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+  for (int c = 0; c < n_chunks; ++c) {
+    if ((long long)n * l_k_chunks[c] == 0) continue;
+    int dlo, dhi;
+    mask_bounds(causal, win_l, win_r, q_offset, k_offsets[c], &dlo, &dhi);
+    ch[m++] = bea::FwdChunk{static_cast<const uint16_t*>(k_chunks[c]),
+                            static_cast<const uint16_t*>(v_chunks[c]), l_k_chunks[c], dlo, dhi};
+  }
+  // no keys at all: every row is empty, O = 0 and LSE = -inf
+  if (m == 0)
+    return finish(bea::launch_acc_init(static_cast<float*>(out), lse, n, l_q, h, d / 2, hs));
+  s.l_k = ch[0].l_k;
+  s.dlo = ch[0].dlo;
+  s.dhi = ch[0].dhi;
+  return finish(bea::launch_fwd_pipe(q, ch, m, out, lse, s, hs));
 }
 
 int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,

@@ -785,6 +785,23 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
   return hipGetLastError();
 }
 
+const char* fwd_bf16_kernel_name(const AttnShape& s, bool acc) {
+  FwdParams p;
+  p.l_q = s.l_q;
+  p.l_k = s.l_k;
+  p.n_heads = s.n * s.h;
+  p.n_qtiles = (s.l_q + kBM - 1) / kBM;
+  p.dlo = s.dlo;
+  p.dhi = s.dhi;
+  const int split = pick_schedule(p) != FwdSchedule::kOneGroup ? 1 : 0;
+  static const char* const names[2][2][2] = {
+      {{"fwd_bf16_kernel<64, 64, 1, false>", "fwd_bf16_kernel<64, 64, 1, true>"},
+       {"fwd_bf16_kernel<64, 64, 2, false>", "fwd_bf16_kernel<64, 64, 2, true>"}},
+      {{"fwd_bf16_kernel<128, 64, 1, false>", "fwd_bf16_kernel<128, 64, 1, true>"},
+       {"fwd_bf16_kernel<128, 64, 2, false>", "fwd_bf16_kernel<128, 64, 2, true>"}}};
+  return names[s.d == 128 ? 1 : 0][split][acc ? 1 : 0];
+}
+
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
                           void* out, float* lse, const AttnShape& s,
                           hipStream_t stream) {

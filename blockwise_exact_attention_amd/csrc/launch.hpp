@@ -4,8 +4,20 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace bea {
+
+// One key/value chunk of a forward call: its tensors [n, l_k, h_kv, d]
+// (bf16) and the mask bounds of its keys (allowed iff dlo <= j - i <= dhi
+// and j < l_k, j counted within the chunk).
+constexpr int kMaxChunks = 16;
+struct FwdChunk {
+  const uint16_t* k;
+  const uint16_t* v;
+  int l_k;
+  int dlo, dhi;
+};
 
 struct AttnShape {
   int n, l_q, l_k, h, h_kv, d;
@@ -20,6 +32,21 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v,
                            void* out, float* lse, const AttnShape& s,
                            hipStream_t stream, float* acc = nullptr,
                            float* lse_acc = nullptr);
+// The software-pipelined bf16 forward over n_chunks (1..kMaxChunks) key
+// chunks visited in order by one online softmax; acc != nullptr merges the
+// result into the fp32 accumulator (one chunk only).  force_ksplit 1 or 2 overrides the
+// schedule choice (0: choose).
+hipError_t launch_fwd_pipe(const void* q, const FwdChunk* chunks, int n_chunks, void* out,
+                           float* lse, const AttnShape& s, hipStream_t stream,
+                           float* acc = nullptr, float* lse_acc = nullptr,
+                           int force_ksplit = 0);
+// Whether the pipelined kernel is the faster one for these chunks (long key
+// loops per q tile); otherwise launch_fwd_bf16 is.
+bool fwd_pipe_preferred(const FwdChunk* chunks, int n_chunks, const AttnShape& s);
+// Names of the kernel instantiations the launchers above would choose.
+const char* fwd_bf16_kernel_name(const AttnShape& s, bool acc);
+const char* fwd_pipe_kernel_name(const FwdChunk* chunks, int n_chunks, const AttnShape& s,
+                                 bool acc);
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
                           void* out, float* lse, const AttnShape& s,
                           hipStream_t stream);

@@ -73,10 +73,11 @@ enum attn_status {
   ATTN_ERR_NULL = 1,        /* a pointer to a non-empty tensor is NULL           */
   ATTN_ERR_SHAPE = 2,       /* a size is negative, h, h_kv or d is 0,
                                h % h_kv != 0, sizes overflow, a row of q
-                               (h * d) exceeds 32 MiB in float32, or a grid
-                               would exceed 2^31 workgroups                      */
+                               (h * d) exceeds 32 MiB in float32, a grid
+                               would exceed 2^31 workgroups, or a chunk count
+                               outside 1..ATTN_RING_MAX_CHUNKS                   */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite
-                               scale, or fp32 backward / fused ring step         */
+                               scale, or fp32 backward / ring step / ring share  */
   ATTN_ERR_HIP = 4,         /* the HIP runtime reported a launch failure         */
   ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than required (or NULL when
                                required)                                         */
@@ -153,6 +154,50 @@ int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
                  float* lse_acc, int n, int l_q, int l_k, int h, int h_kv, int d,
                  float scale, int causal, int win_l, int win_r,
                  long long q_offset, long long k_offset, void* stream, int dtype);
+
+/*
+ * attn_fwd_kernel_name - which kernel attn_fwd (fused = 0) or attn_fwd_acc
+ * (fused = 1) launches for these arguments: the template instantiation as
+ * kernel traces name it (a static string), or NULL when the call would be
+ * rejected or would launch no attention kernel (no rows or no keys).  For
+ * profiling and reports; launches nothing.
+ */
+const char* attn_fwd_kernel_name(int n, int l_q, int l_k, int h, int h_kv, int d,
+                                 float scale, int causal, int win_l, int win_r,
+                                 long long q_offset, long long k_offset, int dtype,
+                                 int fused);
+
+/*
+ * attn_fwd_ring - one device's whole ring-attention share in one launch
+ * (flash_sharding.py ring_fwd: the loop over the key/value chunks that pass
+ * around the ring, each attended with its own absolute offset and merged
+ * into the running (O, LSE); picotron RingAttentionFunc.forward).  The
+ * online softmax runs across the chunks in the order given, so no
+ * accumulator leaves the registers: the result is attn_fwd over the keys of
+ * all chunks together, key j of chunk c at absolute position
+ * k_offsets[c] + j (what attn_acc_init, attn_fwd_acc per chunk and
+ * attn_acc_cast give, up to rounding order).
+ *
+ *   q            [n,l_q,h,d]     in   bfloat16 (dtype must be ATTN_BF16)
+ *   k_chunks[c], v_chunks[c]
+ *                [n,l_k_chunks[c],h_kv,d]  in  bfloat16, device pointers
+ *   k_chunks, v_chunks, l_k_chunks, k_offsets: host arrays of n_chunks
+ *                entries, read during the call only
+ *   out          [n,l_q,h,d]     out  bfloat16
+ *   lse          [n,h,l_q]       out  float32, natural log, -inf for rows
+ *                with no allowed key in any chunk (O = 0 there)
+ *   1 <= n_chunks <= ATTN_RING_MAX_CHUNKS (else ATTN_ERR_SHAPE); a chunk may
+ *   have l_k_chunks[c] = 0 (it adds nothing); d in {64, 128}; masking as for
+ *   attn_fwd with q_offset and each chunk's k_offsets[c].
+ * out and lse must not overlap q or any chunk.  Each chunk is checked as
+ * attn_fwd checks k and v.
+ */
+#define ATTN_RING_MAX_CHUNKS 16
+int attn_fwd_ring(const void* q, const void* const* k_chunks, const void* const* v_chunks,
+                  const int* l_k_chunks, const long long* k_offsets, int n_chunks,
+                  void* out, float* lse, int n, int l_q, int h, int h_kv, int d,
+                  float scale, int causal, int win_l, int win_r, long long q_offset,
+                  void* stream, int dtype);
 
 /*
  * attn_acc_init - set a ring accumulator to the empty result, O = 0 and

@@ -2,6 +2,7 @@
 every function the header declares, and rejects bad arguments before making
 any HIP call.  Pointers here are fake addresses: each call must fail its
 argument checks, so nothing is ever dereferenced or launched."""
+import ctypes
 import os
 import re
 
@@ -35,7 +36,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_fwd_acc", "attn_merge", "attn_bwd",
+    for n in ("attn_fwd", "attn_fwd_acc", "attn_fwd_ring", "attn_merge", "attn_bwd",
               "attn_bwd_acc", "attn_acc_init", "attn_acc_cast",
               "attn_bwd_workspace_bytes", "attn_status_string"):
         assert n in names
@@ -54,6 +55,8 @@ def test_python_constants_match_the_header():
     assert len(consts) == 10
     for name, value in consts.items():
         assert getattr(_lib, name) == value, name
+    defines = dict(re.findall(r"#define\s+(ATTN_\w+)\s+(\d+)", text))
+    assert int(defines["ATTN_RING_MAX_CHUNKS"]) == _lib.ATTN_RING_MAX_CHUNKS
 
 
 def test_status_strings():
@@ -99,6 +102,58 @@ def test_fwd_acc_argument_checks():
     assert _fwd_acc(acc=A + 64) == ATTN_ERR_ALIAS
     assert _fwd_acc(lse=D_ + 1024) == ATTN_ERR_ALIAS
     assert _fwd_acc(lse=C + 16) == ATTN_ERR_ALIAS
+
+
+def _fwd_ring(chunks=None, **kw):
+    """chunks: list of (k, v, l_k, k_offset); default two chunks of 128 keys
+    at B/C and F/F+2^30."""
+    a = dict(q=A, out=D_, lse=E, n=1, l_q=128, h=2, h_kv=2, d=64, scale=0.125,
+             causal=0, win_l=-1, win_r=-1, q_offset=0, stream=None, dtype=ATTN_BF16,
+             n_chunks=None, arrays=True)
+    a.update(kw)
+    if chunks is None:
+        chunks = [(B, C, 128, 0), (F, F + (1 << 30), 128, 128)]
+    nc = len(chunks) if a["n_chunks"] is None else a["n_chunks"]
+    m = max(len(chunks), 1)
+    kp = (ctypes.c_void_p * m)(*[c[0] for c in chunks])
+    vp = (ctypes.c_void_p * m)(*[c[1] for c in chunks])
+    lk = (ctypes.c_int * m)(*[c[2] for c in chunks])
+    ko = (ctypes.c_longlong * m)(*[c[3] for c in chunks])
+    if not a["arrays"]:
+        kp = None
+    return _lib.lib().attn_fwd_ring(a["q"], kp, vp, lk, ko, nc, a["out"], a["lse"],
+                                    a["n"], a["l_q"], a["h"], a["h_kv"], a["d"],
+                                    a["scale"], a["causal"], a["win_l"], a["win_r"],
+                                    a["q_offset"], a["stream"], a["dtype"])
+
+
+def test_fwd_ring_argument_checks():
+    """The one-launch share checks the chunk count, the host arrays and every
+    chunk as attn_fwd checks k and v, before any HIP call."""
+    assert _fwd_ring(n_chunks=0) == ATTN_ERR_SHAPE
+    many = [(B, C, 16, 16 * i) for i in range(_lib.ATTN_RING_MAX_CHUNKS + 1)]
+    assert _fwd_ring(many) == ATTN_ERR_SHAPE
+    assert _fwd_ring(arrays=False) == ATTN_ERR_NULL
+    for f in ("q", "out", "lse"):
+        assert _fwd_ring(**{f: None}) == ATTN_ERR_NULL
+    assert _fwd_ring([(B, C, 128, 0), (None, C, 128, 0)]) == ATTN_ERR_NULL
+    assert _fwd_ring([(B, C, 128, 0), (F, None, 128, 0)]) == ATTN_ERR_NULL
+    assert _fwd_ring([(B, C, 128, 0), (F, F + 4096, -1, 0)]) == ATTN_ERR_SHAPE
+    assert _fwd_ring(h=6, h_kv=4) == ATTN_ERR_SHAPE
+    assert _fwd_ring(d=96) == ATTN_ERR_UNSUPPORTED
+    assert _fwd_ring(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    assert _fwd_ring(scale=float("nan")) == ATTN_ERR_UNSUPPORTED
+    assert _fwd_ring(out=D_ + 8) == ATTN_ERR_ALIGN
+    assert _fwd_ring([(B, C, 128, 0), (F + 8, F + 4096, 128, 0)]) == ATTN_ERR_ALIGN
+    assert _fwd_ring(out=A + 64) == ATTN_ERR_ALIAS
+    assert _fwd_ring(lse=D_ + 64) == ATTN_ERR_ALIAS
+    # out over the second chunk's v
+    assert _fwd_ring(out=F + (1 << 30) + 64) == ATTN_ERR_ALIAS
+    # no rows: valid, nothing launched, chunk pointers may then be anything
+    assert _fwd_ring(l_q=0, q=None, out=None, lse=None) == ATTN_OK
+    # an empty chunk needs no pointers (rows are still there: checked only
+    # up to the launch, so use zero rows to stay on the host)
+    assert _fwd_ring([(None, None, 0, 0)], l_q=0, q=None, out=None, lse=None) == ATTN_OK
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "out", "lse"])
@@ -346,3 +401,24 @@ def test_bwd_wrapper_consistent_host_tensors_reach_the_device_check(acc):
     with pytest.raises(ValueError, match="GPU"):
         fn(t["dout"], t["q"], t["k"], t["v"], t["out"], t["lse"], t["dq"], t["dk"],
            t["dv"], 0.125, True)
+
+
+def test_fwd_kernel_name_reports_the_dispatch():
+    """Host-side dispatch: short key loops run the one-phase kernel, long
+    ones (64 and more key tiles per q tile on average) the pipelined one;
+    rejected or kernel-free calls name nothing."""
+    from blockwise_exact_attention_amd.attention import fwd_kernel_name
+    import torch
+    assert fwd_kernel_name(2, 2048, 2048, 16, 16, 128, True).startswith("fwd_bf16_kernel<128")
+    assert fwd_kernel_name(4, 4096, 4096, 16, 16, 64, True, 256, 0).startswith(
+        "fwd_bf16_kernel<64")
+    assert fwd_kernel_name(1, 16384, 16384, 16, 16, 128, True).startswith("fwd_pipe_kernel<128")
+    assert fwd_kernel_name(1, 1024, 8192, 32, 8, 128, True, q_offset=7168).startswith(
+        "fwd_pipe_kernel<128")
+    assert fwd_kernel_name(1, 1024, 1024, 32, 8, 128, True, q_offset=7168,
+                           fused=True).endswith("true>")
+    assert fwd_kernel_name(1, 128, 128, 2, 2, 64, dtype=torch.float32) == "fwd_f32_kernel<64>"
+    assert fwd_kernel_name(1, 128, 128, 2, 2, 64, dtype=torch.float32, fused=True) is None
+    assert fwd_kernel_name(1, 0, 128, 2, 2, 64) is None
+    assert fwd_kernel_name(1, 128, 0, 2, 2, 64) is None
+    assert fwd_kernel_name(1, 128, 128, 2, 2, 96) is None

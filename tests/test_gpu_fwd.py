@@ -72,12 +72,12 @@ def test_c3_ring_share():
     ro, rl = oracle.attention_fwd(q_full_rows, x["k_full"], x["v_full"],
                                   w.softmax_scale, True, -1, -1,
                                   x["q_offset"], 0, heads=heads, block=1024)
-    for fused in (False, True):
-        out, lse_acc = share.run(kc, vc, x["k_offsets"], fused=fused)
+    for fused, one in ((False, False), (True, False), (False, True)):
+        out, lse_acc = share.run(kc, vc, x["k_offsets"], fused=fused, one_launch=one)
         torch.cuda.synchronize()
         o, lse = host(out), host(lse_acc)
         check_o_lse(o, lse, ro, rl, "bf16",
-                    f"C3 ring share (fused={fused}) vs full-sequence rows")
+                    f"C3 ring share (fused={fused}, one launch={one}) vs full-sequence rows")
     # the all-gather form: the chunks side by side, one call with the offset
     o, lse = run_fwd(x["q"], x["k_full"], x["v_full"], "bf16", w.softmax_scale,
                      True, -1, -1, x["q_offset"], 0)
