@@ -236,18 +236,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     const int n_g = (total - grp + KSPLIT - 1) / KSPLIT;   // this group's tiles
     const int n_steps = (total + KSPLIT - 1) / KSPLIT;     // group 0's (the most)
 
-    // ---- buffer resource of one K or V tile (virtual index v); past the
-    // last tile a zero-length range, whose loads write zeros into a buffer
-    // nobody reads
-    auto kv_rsrc = [&](int v, bool is_v) {
+    // ---- cursor over the virtual tiles: chunk c, tile kt within it, and
+    // the end of the chunk's span for this q tile.  Valid while kt < end (a
+    // cursor only stops short of its chunk's end in the last chunk).  The
+    // key loop moves each cursor KSPLIT tiles per step, crossing into the
+    // next chunks with non-empty spans: constant scalar work per step.
+    struct Cur {
+      int c, kt, end;
+    };
+    auto cur_at = [&](int v) {
+      const TileRef t = locate<MULTI>(p, v, i0, i_last);
+      const TileSpan sp = chunk_span(p.ch[t.c], i0, i_last);
+      return Cur{t.c, t.kt, sp.beg + sp.cnt};
+    };
+    auto cur_next = [&](Cur x) {
+      x.kt += KSPLIT;
+      if (MULTI) {
+        while (x.kt >= x.end && x.c + 1 < p.n_chunks) {
+          const int over = x.kt - x.end;
+          ++x.c;
+          const TileSpan sp = chunk_span(p.ch[x.c], i0, i_last);
+          x.kt = sp.beg + over;
+          x.end = sp.beg + sp.cnt;
+        }
+      }
+      return x;
+    };
+
+    // ---- buffer resource of one K or V tile; past the last tile a
+    // zero-length range, whose loads write zeros into a buffer nobody reads
+    auto kv_rsrc = [&](const Cur& x, bool is_v) {
       int bytes = 0;
       const uint16_t* base = p.ch[0].k;
-      if (v < total) {
-        const TileRef t = locate<MULTI>(p, v, i0, i_last);
-        const FwdChunk& ch = p.ch[t.c];
-        const long long rows = (long long)ch.l_k - (long long)t.kt * kBN;
+      if (x.kt < x.end) {
+        const FwdChunk& ch = p.ch[x.c];
+        const long long rows = (long long)ch.l_k - (long long)x.kt * kBN;
         bytes = (int)min(rows * (long long)kv_row_b, 0x7fffffffLL);
-        base = (is_v ? ch.v : ch.k) + ((size_t)b * ch.l_k + (size_t)t.kt * kBN) * kv_row +
+        base = (is_v ? ch.v : ch.k) + ((size_t)b * ch.l_k + (size_t)x.kt * kBN) * kv_row +
                (size_t)g * D;
       }
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes,
@@ -275,8 +300,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
 
     // ---- prologue: Q tile, K and V of the first tile, K of the second
     dma_q();
+    // cursors of this group's first tile, of the tile whose V (and mask) the
+    // first step needs, and of the tile whose K it loads
+    const Cur cur0 = cur_at(grp);
+    Cur curV = cur_next(cur0);
+    Cur curK = cur_next(curV);
     if (n_g > 0) {
-      const auto rk = kv_rsrc(grp, false), rv = kv_rsrc(grp, true);
+      const auto rk = kv_rsrc(cur0, false), rv = kv_rsrc(cur0, true);
 #pragma unroll
       for (int x = 0; x < KV_DMA; ++x) {
         dma_kv(rk, k_lds0[grp], x);
@@ -284,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       }
     }
     if (n_g > 1) {
-      const auto rk = kv_rsrc(grp + KSPLIT, false);
+      const auto rk = kv_rsrc(curV, false);
 #pragma unroll
       for (int x = 0; x < KV_DMA; ++x) dma_kv(rk, k_lds1[grp], x);
     }
@@ -323,11 +353,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       bool full;
       int j0, l_k, dlo, dhi;
     };
-    auto tile_info = [&](int v) {
-      const TileRef t = locate<MULTI>(p, v, i0, i_last);
-      const FwdChunk& ch = p.ch[t.c];
+    auto tile_info = [&](const Cur& x) {
+      const FwdChunk& ch = p.ch[x.c];
       TileInfo ti;
-      ti.j0 = t.kt * kBN;
+      ti.j0 = x.kt * kBN;
       ti.l_k = ch.l_k;
       ti.dlo = ch.dlo;
       ti.dhi = ch.dhi;
@@ -484,12 +513,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
 
     // ---- phase 1: S_next = K Q^T (when `next`) beside the exponentials of T
     auto phase1 = [&](bool next, f32x16_t (&Snext)[NKB], f32x16_t (&T)[NKB],
-                      const unsigned char* kl, int v_dma_k, unsigned char* kdst, int v_dma_v,
-                      unsigned char* vdst) {
+                      const unsigned char* kl, unsigned char* kdst, unsigned char* vdst) {
       __amdgpu_buffer_rsrc_t rk, rv;
       if (next) {
-        rk = kv_rsrc(v_dma_k, false);
-        rv = kv_rsrc(v_dma_v, true);
+        rk = kv_rsrc(curK, false);
+        rv = kv_rsrc(curV, true);
       }
       SoftB z;
       z.rs = 0.f;
@@ -573,7 +601,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
                                                              kb * 32 * RB);
           sA[kb] = mfma32x32x16(a, qf[s], s == 0 ? f32x16_t{} : sA[kb]);
         }
-      const TileInfo ti = tile_info(grp);
+      const TileInfo ti = tile_info(cur0);
       if (!ti.full) apply_mask(sA, tile_bits(ti));
       SoftA z;
 #pragma unroll
@@ -587,20 +615,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     // straight-line body (only the boundary mask and the rare rescale
     // branch); the last step and the idle steps of a group with one tile
     // fewer follow the loop.
-    auto step_next = [&](int u, f32x16_t (&T)[NKB], f32x16_t (&Sn)[NKB],
-                         const unsigned char* kl, const unsigned char* vl, unsigned char* kdst,
-                         unsigned char* vdst) {
-      const int vn = grp + KSPLIT * (u + 1);
-      phase1(true, Sn, T, kl, grp + KSPLIT * (u + 2), kdst, vn, vdst);
-      const TileInfo ti = tile_info(vn);
+    auto step_next = [&](f32x16_t (&T)[NKB], f32x16_t (&Sn)[NKB], const unsigned char* kl,
+                         const unsigned char* vl, unsigned char* kdst, unsigned char* vdst) {
+      // loads: K of the tile after next (curK), V of the next (curV)
+      phase1(true, Sn, T, kl, kdst, vdst);
+      const TileInfo ti = tile_info(curV);
       if (!ti.full) apply_mask(Sn, tile_bits(ti));
       phase2(true, Sn, vl);
       rescale_o();
+      curV = curK;
+      curK = cur_next(curK);
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads landed
       __syncthreads();
     };
     auto step_last = [&](f32x16_t (&T)[NKB], f32x16_t (&Sn)[NKB], const unsigned char* vl) {
-      phase1(false, Sn, T, nullptr, 0, nullptr, 0, nullptr);
+      phase1(false, Sn, T, nullptr, nullptr, nullptr);
       phase2(false, Sn, vl);
       __syncthreads();
     };
@@ -610,11 +639,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     const int n_next = n_g - 1;   // steps with a next tile
     int u = 0;
     for (; u + 1 < n_next; u += 2) {
-      step_next(u, sA, sB, &k_lds1[0][0], &v_lds0[0][0], k_lds0[grp], v_lds1[grp]);
-      step_next(u + 1, sB, sA, &k_lds0[0][0], &v_lds1[0][0], k_lds1[grp], v_lds0[grp]);
+      step_next(sA, sB, &k_lds1[0][0], &v_lds0[0][0], k_lds0[grp], v_lds1[grp]);
+      step_next(sB, sA, &k_lds0[0][0], &v_lds1[0][0], k_lds1[grp], v_lds0[grp]);
     }
     if (u < n_next) {
-      step_next(u, sA, sB, &k_lds1[0][0], &v_lds0[0][0], k_lds0[grp], v_lds1[grp]);
+      step_next(sA, sB, &k_lds1[0][0], &v_lds0[0][0], k_lds0[grp], v_lds1[grp]);
       ++u;
     }
     if (n_g > 0) {
