@@ -21,6 +21,7 @@ ATTN_F32 = 0
 ATTN_BF16 = 1
 
 ATTN_RING_MAX_CHUNKS = 16
+ATTN_BWD_STATIC_MAX_WORKSPACE = 64 << 20
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -44,6 +45,8 @@ SIGNATURES = {
                       _i, _i, _i, _f, _i, _i, _i, _ll, _ll, _vp, _sz, _vp, _i]),
     "attn_bwd_acc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
                           _i, _i, _i, _f, _i, _i, _i, _ll, _ll, _vp, _sz, _vp, _i]),
+    "attn_bwd_static": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                             _i, _i, _i, _f, _i, _i, _i, _ll, _ll, _vp, _i]),
     "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
 }

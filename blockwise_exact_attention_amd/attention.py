@@ -289,6 +289,25 @@ def attn_bwd_acc(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, scale,
     return dq_acc, dk_acc, dv_acc
 
 
+def attn_bwd_static(dout, q, k, v, out, lse, dq, dk, dv, scale, causal=False,
+                    win_l=-1, win_r=-1, q_offset=0, k_offset=0, stream=None):
+    """attn_bwd with the library's static per-device workspace: allocates
+    nothing.  Calls that overlap in time on one device race (they share the
+    workspace)."""
+    _check_bwd(dout, q, k, v, out, lse, dq, dk, dv, acc=False)
+    n, l_q, h, d = q.shape
+    _, l_k, h_kv, _ = k.shape
+    st = _lib.lib().attn_bwd_static(dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                    v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), n,
+                                    l_q, l_k, h, h_kv, d, float(scale),
+                                    int(bool(causal)), int(win_l), int(win_r),
+                                    int(q_offset), int(k_offset), _stream(stream),
+                                    _dtype_code(q))
+    check("attn_bwd_static", st)
+    return dq, dk, dv
+
+
 def attention_backward(dout, q, k, v, out, lse, scale=None, causal=False,
                        window=(-1, -1), q_offset=0, k_offset=0, stream=None):
     if scale is None:

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn.h"
 #include "launch.hpp"
 
@@ -317,15 +319,54 @@ size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv,
 
 namespace {
 
-// Shared by attn_bwd and attn_bwd_acc: argument checks (gradient outputs of
-// gb bytes per element), then the launch; acc selects the accumulating
-// kernels (gradients added to fp32 dq, dk, dv).
+// Workspace of attn_bwd_static: one copy per device, held from the first
+// load of the library's code object on that device until the process ends.
+// Host code never passes `scratch` itself to a kernel or a copy (on the
+// host the name is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+constexpr size_t kScratchBytes = (size_t)ATTN_BWD_STATIC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the device `stream` belongs to (the current device
+// for the null stream), looked up once per device with that device current.
+int scratch_for_stream(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (stream == nullptr) {
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  } else if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    return ATTN_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return ATTN_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+// Shared by attn_bwd, attn_bwd_acc and attn_bwd_static: argument checks
+// (gradient outputs of gb bytes per element), then the launch; acc selects
+// the accumulating kernels (gradients added to fp32 dq, dk, dv);
+// use_scratch takes the workspace from the device's static scratch instead
+// of the caller (workspace and workspace_bytes are then ignored).
 int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
               const void* out, const float* lse, void* dq, void* dk, void* dv,
               int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
               int causal, int win_l, int win_r, long long q_offset,
               long long k_offset, void* workspace, size_t workspace_bytes,
-              void* stream, int dtype, bool acc) {
+              void* stream, int dtype, bool acc, bool use_scratch = false) {
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
@@ -340,8 +381,12 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
     return ATTN_ERR_NULL;
   const bool empty = qe == 0 || ke == 0;
   const size_t need = empty ? 0 : bea::bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d);
-  if (missing(workspace, (long long)need) || workspace_bytes < need)
+  if (use_scratch) {
+    if (need > kScratchBytes) return ATTN_ERR_WORKSPACE;
+    workspace = nullptr;   // set after the checks
+  } else if (missing(workspace, (long long)need) || workspace_bytes < need) {
     return ATTN_ERR_WORKSPACE;
+  }
   if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(k, 16) ||
       !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
@@ -349,8 +394,9 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
     return ATTN_ERR_ALIGN;
   const Range ins[] = {range(dout, qe * es), range(q, qe * es), range(k, ke * es),
                        range(v, ke * es), range(out, qe * es), range(lse, lb)};
+  // the static scratch is the library's own memory: no caller buffer meets it
   const Range outs[] = {range(dq, qe * gb), range(dk, ke * gb), range(dv, ke * gb),
-                        range(workspace, (long long)need)};
+                        range(workspace, use_scratch ? 0LL : (long long)need)};
   for (int a = 0; a < 4; ++a) {
     for (const Range& r : ins)
       if (overlap(outs[a], r)) return ATTN_ERR_ALIAS;
@@ -359,6 +405,10 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
   }
   (void)hipGetLastError();
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (use_scratch && need > 0) {
+    st = scratch_for_stream(hs, &workspace);
+    if (st != ATTN_OK) return st;
+  }
   if (empty) {
     // No queries or no keys: every gradient is zero.  The accumulating form
     // adds nothing; the plain form clears the non-empty gradients (as 32-bit
@@ -408,6 +458,16 @@ int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
   return bwd_entry(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, n, l_q, l_k, h,
                    h_kv, d, scale, causal, win_l, win_r, q_offset, k_offset,
                    workspace, workspace_bytes, stream, dtype, true);
+}
+
+int attn_bwd_static(const void* dout, const void* q, const void* k, const void* v,
+                    const void* out, const float* lse, void* dq, void* dk, void* dv, int n,
+                    int l_q, int l_k, int h, int h_kv, int d, float scale, int causal,
+                    int win_l, int win_r, long long q_offset, long long k_offset,
+                    void* stream, int dtype) {
+  return bwd_entry(dout, q, k, v, out, lse, dq, dk, dv, n, l_q, l_k, h, h_kv, d, scale,
+                   causal, win_l, win_r, q_offset, k_offset, nullptr, 0, stream, dtype,
+                   false, true);
 }
 
 const char* attn_status_string(int status) {

@@ -273,6 +273,30 @@ int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
  * partials (summed in a fixed order, so results stay bitwise repeatable). */
 size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);
 
+/*
+ * attn_bwd_static - attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, with the workspace taken
+ * from a static array of ATTN_BWD_STATIC_MAX_WORKSPACE bytes that the
+ * library holds on each device it runs on until the process ends.  The
+ * call allocates and frees nothing.
+ *
+ *   Arguments as for attn_bwd, without workspace and workspace_bytes.
+ *   Returns ATTN_ERR_WORKSPACE when attn_bwd_workspace_bytes(...) for these
+ *   sizes exceeds ATTN_BWD_STATIC_MAX_WORKSPACE (nothing is launched), and
+ *   ATTN_ERR_HIP when the device of `stream` cannot be queried.
+ * Every call on one device shares that device's array: calls that overlap
+ * in time on one device (different streams without ordering between them,
+ * or different host threads) race and give wrong gradients.  Order them on
+ * one stream, or use attn_bwd with a workspace per stream.
+ */
+#define ATTN_BWD_STATIC_MAX_WORKSPACE (64 << 20)
+int attn_bwd_static(const void* dout, const void* q, const void* k, const void* v,
+                    const void* out, const float* lse, void* dq, void* dk, void* dv,
+                    int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
+                    int causal, int win_l, int win_r, long long q_offset,
+                    long long k_offset, void* stream, int dtype);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(int status);
 

@@ -55,8 +55,10 @@ def test_python_constants_match_the_header():
     assert len(consts) == 10
     for name, value in consts.items():
         assert getattr(_lib, name) == value, name
-    defines = dict(re.findall(r"#define\s+(ATTN_\w+)\s+(\d+)", text))
+    defines = dict(re.findall(r"#define\s+(ATTN_\w+)\s+(.+)", text))
     assert int(defines["ATTN_RING_MAX_CHUNKS"]) == _lib.ATTN_RING_MAX_CHUNKS
+    assert defines["ATTN_BWD_STATIC_MAX_WORKSPACE"].strip() == "(64 << 20)"
+    assert _lib.ATTN_BWD_STATIC_MAX_WORKSPACE == 64 << 20
 
 
 def test_status_strings():
@@ -273,6 +275,37 @@ def test_bwd_checks():
     alias[6] = ptrs[1]          # dq on top of q
     assert call(ptrs=alias) == ATTN_ERR_ALIAS
     assert call(ws=ptrs[7]) == ATTN_ERR_ALIAS   # workspace on top of dk
+
+
+def test_bwd_static_checks():
+    """The allocation-free backward checks what attn_bwd checks, and refuses
+    sizes whose workspace exceeds its static array, before any HIP call."""
+    L = _lib.lib()
+    ptrs = [A, A + (1 << 28), B, B + (1 << 28), C, C + (1 << 28), D_,
+            D_ + (1 << 28), E]
+
+    def call(ptrs=ptrs, n=1, l=128, d=64, h=2, h_kv=2, dtype=ATTN_BF16):
+        return L.attn_bwd_static(*ptrs, n, l, l, h, h_kv, d, 0.125, 1, -1, -1, 0, 0, None,
+                                 dtype)
+    bad = list(ptrs)
+    bad[3] = None
+    assert call(ptrs=bad) == ATTN_ERR_NULL
+    assert call(h=3) == ATTN_ERR_SHAPE
+    assert call(d=32) == ATTN_ERR_UNSUPPORTED
+    assert call(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    alias = list(ptrs)
+    alias[6] = ptrs[1]          # dq on top of q
+    assert call(ptrs=alias) == ATTN_ERR_ALIAS
+    # 2^21 rows of 4 heads: D and LSE take exactly the 64 MiB (accepted, up
+    # to the launch); of 5 heads, 80 MiB (refused)
+    big = [i << 40 for i in range(1, 10)]
+    assert L.attn_bwd_workspace_bytes(1, 1 << 21, 1 << 21, 4, 4, 64) == \
+        _lib.ATTN_BWD_STATIC_MAX_WORKSPACE
+    assert L.attn_bwd_workspace_bytes(1, 1 << 21, 1 << 21, 5, 5, 64) > \
+        _lib.ATTN_BWD_STATIC_MAX_WORKSPACE
+    assert call(ptrs=big, l=1 << 21, h=5, h_kv=5) == ATTN_ERR_WORKSPACE
+    # no rows: nothing to do, no workspace needed
+    assert call(ptrs=[None] * 9, l=0) == ATTN_OK
 
 
 def test_allowed_pairs_matches_oracle_mask():
