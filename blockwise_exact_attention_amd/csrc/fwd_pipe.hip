@@ -11,7 +11,8 @@
 // with their absolute offsets, which the multi-chunk form runs in one
 // launch).
 //
-// Layout (one workgroup of 8 waves per CU, up to 160 KB of LDS):
+// Layout (one workgroup of 8 waves per CU; 132 KB of LDS at KSPLIT = 2,
+// 64 KB at KSPLIT = 1):
 //  * A wave owns 32 query rows of one head.  Scores are computed transposed,
 //    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows from LDS are the A
 //    operand, the wave's Q rows stay in VGPRs as the B operand.  In the
@@ -37,7 +38,8 @@
 //    window edges, ragged ends) get a mask pass before phase 2.
 //  * K and V tiles of 64 keys are double-buffered in LDS and filled by
 //    direct buffer-to-LDS loads; K runs one tile ahead of V.  One barrier
-//    per tile.  The Q tile arrives the same way at the start of a q tile.
+//    per tile.  Each wave loads its Q rows straight into registers at the
+//    start of a q tile, beside the first K/V loads.
 //  * The running max is updated lazily (rescale only when a tile's max
 //    exceeds it by a slack), so O is rarely touched outside the products.
 //  * Normalised O leaves through LDS as row-contiguous stores.  The ACC
@@ -156,7 +158,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
   constexpr int TILE = kBN * RB;
   constexpr int RPD = 1024 / RB;                // rows one wave-wide load writes
   constexpr int KV_DMA = kBN / RPD / WPG;       // loads per wave per K (or V) tile
-  constexpr int Q_DMA = QROWS / RPD / kWaves;   // loads per wave of the Q tile
   constexpr int NKB = 2;         // 32-key blocks per tile
   constexpr int NDS = D / 16;    // S^T MFMA k steps
   constexpr int NDB = D / 32;    // 32-dim blocks of O^T
@@ -164,12 +165,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
   constexpr int NSLOT = NKB * NDS;   // phase-1 slots, one product each
   constexpr int NSLOT2 = NPS * NDB;  // phase-2 slots, one product each
   constexpr uint32_t kVC = D == 128 ? 32u : 16u;
-  static_assert(KV_DMA >= 1 && Q_DMA >= 1, "loads");
+  static_assert(KV_DMA >= 1, "loads");
   // the swizzle repeats every 16 rows: with rows stepping by a multiple of
   // 16 between a wave's loads, one lane offset serves them all
   static_assert((WPG * RPD) % 16 == 0 && (kWaves * RPD) % 16 == 0, "swizzle period");
 
-  __shared__ __attribute__((aligned(16))) unsigned char q_lds[QROWS * RB];
+  // the key groups' (m, l) exchange at the end of a q tile
+  __shared__ float2 xml_lds[KSPLIT == 2 ? kWaves * 64 : 1];
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[KSPLIT][TILE];
   __shared__ __attribute__((aligned(16))) unsigned char k_lds1[KSPLIT][TILE];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[KSPLIT][TILE];
@@ -186,8 +188,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
   uint32_t ka0, va0;
   lds_read_bases<D>(lane, ka0, va0);
   // per-lane LDS byte offsets of the operand reads within a K or V buffer
-  // array, the key group's slot included: every read is then one register
-  // plus an immediate offset (no address arithmetic in the key loop)
+  // array, the key group's slot included: a read is one of these registers
+  // plus the buffer's address and an immediate
   uint32_t kad[NDS], vad[NDB][2];
 #pragma unroll
   for (int s = 0; s < NDS; ++s) kad[s] = (uint32_t)grp * TILE + (ka0 ^ (32u * s));
@@ -215,8 +217,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
   const uint32_t lchunk = (uint32_t)(lane % CPR);
   const uint32_t kv_voff =
       lrow * kv_row_b + ((lchunk ^ chunk_swz<D>((uint32_t)wr * RPD + lrow)) * 16u);
-  const uint32_t q_voff =
-      lrow * q_row_b + ((lchunk ^ chunk_swz<D>((uint32_t)wave_all * RPD + lrow)) * 16u);
 
   // one q tile: prologue, key loop, merge of the key groups, epilogue
   auto fwd_tile = [&](const int tile) {
@@ -284,22 +284,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + row0 * RB), 16, kv_voff,
                                                row0 * kv_row_b, 0, 0);
     };
-    auto dma_q = [&]() {
+
+    // ---- prologue: the wave's Q fragment straight into registers (rows
+    // past the end read as zeros), K and V of the first tile, K of the second.
+    // Lane (col, half) holds row iw + col, dims 16 s + 8 half .. + 7 in qf[s]:
+    // the B operand of the score products, resident for the whole key loop.
+    u32x4_t qf[NDS];
+    {
       const long long rows = (long long)p.l_q - i0;
       const int bytes = (int)min(rows * (long long)q_row_b, 0x7fffffffLL);
       const uint16_t* base = p.q + ((size_t)b * p.l_q + i0) * q_row + (size_t)hq * D;
       const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0,
                                                         bytes, 0x00020000);
+      const uint32_t off = (uint32_t)(wr * 32 + col) * q_row_b + (uint32_t)half * 16u;
 #pragma unroll
-      for (int x = 0; x < Q_DMA; ++x) {
-        const uint32_t row0 = (uint32_t)((x * kWaves + wave_all) * RPD);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(q_lds + row0 * RB), 16,
-                                                 q_voff, row0 * q_row_b, 0, 0);
-      }
-    };
-
-    // ---- prologue: Q tile, K and V of the first tile, K of the second
-    dma_q();
+      for (int s = 0; s < NDS; ++s)
+        qf[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 32u * s), 0, 0);
+    }
     // cursors of this group's first tile, of the tile whose V (and mask) the
     // first step needs, and of the tile whose K it loads
     const Cur cur0 = cur_at(grp);
@@ -321,20 +322,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
 
-    // Q fragment, resident for the whole key loop.  The sign of the scale is
-    // folded into Q (sign-bit flip, exact) and a zero scale becomes Q = 0
-    // with c = log2(e) (every allowed score is then 0, as scale * q.k is), so
-    // c > 0 below and a masked score of -inf always gives exp2(-inf) = 0.
-    u32x4_t qf[NDS];
-    {
-      uint32_t ka = ka0;
-      asm volatile("" : "+v"(ka));
+    // The sign of the scale is folded into Q (sign-bit flip, exact) and a
+    // zero scale becomes Q = 0 with c = log2(e) (every allowed score is then
+    // 0, as scale * q.k is), so c > 0 below and a masked score of -inf
+    // always gives exp2(-inf) = 0.
 #pragma unroll
-      for (int s = 0; s < NDS; ++s)
-        qf[s] = (*reinterpret_cast<const u32x4_t*>(q_lds + wr * 32 * RB + (ka ^ (32u * s))) &
-                 p.q_and) ^
-                p.q_xor;
-    }
+    for (int s = 0; s < NDS; ++s) qf[s] = (qf[s] & p.q_and) ^ p.q_xor;
 
     f32x16_t oacc[NDB];
 #pragma unroll
@@ -495,6 +488,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       z.rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, z.pk[pr]),
                                              __builtin_bit_cast(bf16x2_t, 0x3f803f80u), z.rs,
                                              false);
+      pin(z.rs);   // summed in its slot, not sunk to the end of the step
     };
     auto soft_b = [&](f32x16_t (&T)[NKB], int x, SoftB& z) {
 #pragma unroll
@@ -550,6 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       }
       soft_b_drain(z);
       lsum += z.rs;
+      pin(lsum);
     };
 
     // ---- phase 2: O += P V beside the first softmax half of S_next
@@ -688,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
         float4* base = reinterpret_cast<float4*>(f < NF / 2 ? &v_lds0[0][0] : &v_lds1[0][0]);
         return base[((f % (NF / 2)) * kWaves + w) * 64 + lane];
       };
-      float2* xml = reinterpret_cast<float2*>(q_lds);
+      float2* xml = xml_lds;
       const int partner = (wave_all + WPG) % kWaves;
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -726,15 +721,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     const float lse_b = ltot > 0.f ? (muse + __log2f(ltot)) * kLn2 : kNegInf;
     // this wave's staging slice: 32 rows of the finished dims, in the K
     // buffers (KSPLIT = 2: waves 0-3 in one, 4-7 in the other; the exchange
-    // used the V and Q buffers) or in the Q buffer (KSPLIT = 1); both are
-    // free since the loop ended
+    // used the V buffers) or two waves to each K and V buffer (KSPLIT = 1);
+    // all are free since the loop ended
     unsigned char* stage;
     if constexpr (KSPLIT == 2) {
       static_assert(4 * 32 * RB <= KSPLIT * TILE, "staging fits");
       stage = (wave_all < 4 ? &k_lds0[0][0] : &k_lds1[0][0]) + (wave_all % 4) * 32 * RB;
     } else {
-      static_assert(kWaves * 32 * RB <= QROWS * RB, "staging fits");
-      stage = q_lds + wave_all * 32 * RB;
+      static_assert(2 * 32 * RB <= TILE, "staging fits");
+      const int w2 = wave_all / 2;
+      stage = (w2 == 0 ? &k_lds0[0][0] : w2 == 1 ? &k_lds1[0][0] : w2 == 2 ? &v_lds0[0][0]
+                                                                           : &v_lds1[0][0]) +
+              (wave_all % 2) * 32 * RB;
     }
     if constexpr (ACC) {
       // merge (O / l, LSE) into the accumulator rows (log1p form, the -inf
