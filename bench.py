@@ -1,16 +1,19 @@
 """Benchmark of the blockwise exact-attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extras] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+    python bench.py --workload {c3-steps,c3-fused,c3-share,c3-bwd,c4,c5-fwd,c5-bwd}
 
 Workload: causal multi-head attention, n=2, l=2048, h=h_kv=16, d=128, bf16,
 scale 1/sqrt(128), synthetic N(0,1) inputs resident in HBM.  A step is one
 attn_fwd call over that batch (through the C ABI).  Prints one JSON line:
 forward TFLOP/s (algorithmic FLOPs: 4*d per allowed query/key pair per head),
-the roofline of the forward kernel, and the fp64 CPU oracle's rate on a
-bounded sample of the same workload.  --extras adds the other workloads
-(ring share with its merges, sliding window, long-context forward and
-backward, and the merge's bandwidth warm, cold and on a full-sequence shape)
-as separately timed figures; --merge-only runs just the merge figures.
+the roofline of the forward kernel, the other targeted figures under
+"extras" (the rank-7 ring share as per-chunk forwards, fused steps, one
+launch and backward; the sliding window; the 16k-token forward and backward;
+the merge's bandwidth warm and cold on both shapes against a plain streaming
+copy), and the fp64 CPU oracle's rate on a bounded sample of the headline
+workload.  --workload times one workload's call alone (for profiler runs);
+--merge-only runs just the merge figures.
 """
 from __future__ import annotations
 
@@ -36,7 +39,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--extras", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline workload (and the CPU baseline)")
+    ap.add_argument("--workload", default="c2",
+                    choices=("c2", "c3-steps", "c3-fused", "c3-share", "c3-bwd", "c4",
+                             "c5-fwd", "c5-bwd"),
+                    help="time only this workload's call (for profiler runs); c2 "
+                         "is the default full run")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--oracle-times", action="store_true",
@@ -101,30 +110,37 @@ def cpu_baseline(x, w, seconds):
                       f"{host['usable_cpus']} usable"}
 
 
-KERNEL_SOURCES = ("fwd.hip", "tile.hpp", "common.hpp")
+def kernel_sources(kernel):
+    """The source files a forward kernel is built from."""
+    main = "fwd_pipe.hip" if kernel.startswith("fwd_pipe") else "fwd.hip"
+    return (main, "tile.hpp", "common.hpp", "launch.hpp")
 
 
-def kernel_sources_sha256():
-    """sha256 over the forward kernel's source files, in a fixed order."""
+def kernel_sources_sha256(kernel):
+    """sha256 over a forward kernel's source files, in a fixed order."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in kernel_sources(kernel):
         with open(os.path.join(ROOT, "blockwise_exact_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def counted_traffic():
+COUNTERS_JSON = "fwd_causal_mha_n2_l2048_h16_d128_counters.json"
+
+
+def counted_traffic(kernel):
     """HBM bytes per forward launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or
-    None when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "fwd_bf16_causal_mha_n2_l2048_h16_d128_counters.json")
+    None when that summary is of another kernel or the kernel's sources
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", COUNTERS_JSON)
     try:
         rec = json.load(open(path))
-        sha = kernel_sources_sha256()
+        sha = kernel_sources_sha256(kernel)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sources_sha256") != sha:
+    if rec.get("kernel") != kernel or rec.get("kernel_sources_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -136,9 +152,10 @@ def merge_measurements(A, torch, merge_bytes, steps):
     and 606 MB of distinct memory) that each call's data has left the 256 MB
     Infinity Cache and the L2s since its set was last used, and one event
     pair spans all the calls (a per-call event pair adds microseconds).
-    Warm: one buffer set, merged into again and again.  A plain device copy
-    (torch), cold the same way, is timed beside them as the reference for
-    what a read-and-write stream reaches on this GPU."""
+    Warm: one buffer set, merged into again and again.  The library's plain
+    streaming copy of the same byte count (attn_hbm_copy), cold the same way,
+    is timed beside each as the reference for what a read-and-write stream
+    reaches on this GPU (torch's copy for context)."""
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
@@ -175,18 +192,27 @@ def merge_measurements(A, torch, merge_bytes, steps):
         r["cold_frac_of_hbm"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         res[name] = r
         del sets
-    # reference: a plain device copy (torch), cold the same way
-    for nb, n_sets in ((32 << 20, 16), (1 << 30, 2)):
+    # reference: the library's plain streaming copy (attn_hbm_copy) of the
+    # same number of bytes as each merge moves, cold the same way; torch's
+    # copy beside it for context
+    for name, n_sets in (("ring_block_1x1024x32x128", 16), ("full_sequence_1x8192x32x128", 3)):
+        nb = res[name]["bytes"] // 2 // 16 * 16      # copied once: read nb, write nb
         sets = [(torch.ones(nb // 4, device=dev), torch.empty(nb // 4, device=dev))
                 for _ in range(n_sets)]
-        it = [0]
+        for kind in ("hbm_copy", "torch_copy"):
+            it = [0]
 
-        def copy():
-            src, dst = sets[it[0] % n_sets]
-            dst.copy_(src)
-            it[0] += 1
-        ms = timed(copy, max(4 * n_sets, 32), n_sets, torch)
-        res[f"copy_{nb >> 20}MiB_cold_gbs"] = round(2 * nb / (ms * 1e-3) / 1e9, 1)
+            def copy():
+                src, dst = sets[it[0] % n_sets]
+                if kind == "hbm_copy":
+                    A.hbm_copy(src, dst)
+                else:
+                    dst.copy_(src)
+                it[0] += 1
+            ms = timed(copy, max(4 * n_sets, 32), n_sets, torch)
+            res[name][f"{kind}_cold_gbs"] = round(2 * nb / (ms * 1e-3) / 1e9, 1)
+        res[name]["merge_frac_of_hbm_copy"] = round(
+            res[name]["cold_gbs"] / res[name]["hbm_copy_cold_gbs"], 4)
         del sets
     torch.cuda.empty_cache()
     return res
@@ -313,6 +339,17 @@ def main():
         print(json.dumps({"merge": merge_measurements(A, torch, merge_bytes,
                                                       args.steps)}), flush=True)
         return
+    if args.workload != "c2":
+        # one workload's timed loop alone (for profiler runs)
+        fn, flops, what = single_workload(args.workload, A, torch, allowed_pairs,
+                                          fwd_flops, bwd_flops, WORKLOADS, make_inputs)
+        ms = timed(fn, args.steps, args.warmup, torch)
+        print(json.dumps({"workload": args.workload, "what": what, "steps": args.steps,
+                          "ms": round(ms, 5),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                          "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12
+                                                     / PEAK_BF16_TFLOPS, 4)}), flush=True)
+        return
 
     w = WORKLOADS["C2"]
     x = make_inputs(w)
@@ -323,6 +360,7 @@ def main():
     lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
     pairs = allowed_pairs(w.l_q, w.l_k, True)
     flops = fwd_flops(w.n, w.h, w.d, pairs)
+    kernel = A.fwd_kernel_name(w.n, w.l_q, w.l_k, w.h, w.h_kv, w.d, True)
 
     def step():
         A.attn_fwd(tq, tk, tv, out, lse, w.softmax_scale, True)
@@ -369,14 +407,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": counted_traffic(),
-                     "kernel": "fwd_bf16_kernel<128, 64, 2, false>",
+                     "traffic": counted_traffic(kernel),
+                     "kernel": kernel,
                      "kernel_ms_per_launch": round(kern_ms, 5),
                      "algorithmic_bytes": fwd_bytes(w.n, w.l_q, w.l_k, w.h,
                                                     w.h_kv, w.d, 2)},
     }
+    del tq, tk, tv, out, lse
 
-    if args.extras:
+    if not args.no_extras:
         rec["extras"] = extras(A, torch, args, allowed_pairs, fwd_flops,
                                bwd_flops, merge_bytes, WORKLOADS, make_inputs)
     if not args.no_cpu:
@@ -384,39 +423,111 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+def _frac(tflops):
+    return round(tflops / PEAK_BF16_TFLOPS, 4)
+
+
+def _dev_bf16(torch, a):
+    return torch.from_numpy(a).to(torch.bfloat16).to(torch.device("cuda:0"))
+
+
+def single_workload(name, A, torch, allowed_pairs, fwd_flops, bwd_flops, WORKLOADS,
+                    make_inputs):
+    """(callable, algorithmic FLOPs per call, description) of one workload's
+    timed call, inputs resident on the GPU."""
+    t = lambda a: _dev_bf16(torch, a)
+    dev = torch.device("cuda:0")
+    if name.startswith("c3"):
+        w = WORKLOADS["C3"]
+        x = make_inputs(w)
+        tq = t(x["q"])
+        kc = [t(c) for c in x["k_chunks"]]
+        vc = [t(c) for c in x["v_chunks"]]
+        offs = x["k_offsets"]
+        pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, x["q_offset"], ko) for ko in offs)
+        share = A.RingShare(tq, w.softmax_scale, True, x["q_offset"])
+        if name == "c3-steps":
+            def fn():
+                for s in range(8):
+                    A.attn_fwd(tq, kc[s], vc[s], share.blk, share.lse_blk, w.softmax_scale,
+                               True, -1, -1, x["q_offset"], offs[s])
+            return fn, fwd_flops(1, 32, 128, pairs), "the 8 per-chunk forwards of the rank-7 share"
+        if name == "c3-fused":
+            return (lambda: share.run(kc, vc, offs, fused=True), fwd_flops(1, 32, 128, pairs),
+                    "rank-7 share as 8 fused steps (init, 8 x attn_fwd_acc, cast)")
+        if name == "c3-share":
+            return (lambda: share.run(kc, vc, offs, one_launch=True),
+                    fwd_flops(1, 32, 128, pairs), "rank-7 share in one attn_fwd_ring launch")
+        if name == "c3-bwd":
+            tdo = t(np.random.default_rng(77).standard_normal(x["q"].shape).astype(np.float32))
+            o, l = share.run(kc, vc, offs, one_launch=True)
+            b = A.RingShareBwd(tq, o.clone(), l.clone(), tdo, w.softmax_scale, True,
+                               x["q_offset"])
+            return (lambda: b.run(kc, vc, offs), bwd_flops(1, 32, 128, pairs),
+                    "rank-7 ring backward share")
+    if name == "c4":
+        w = WORKLOADS["C4"]
+        x = make_inputs(w)
+        tq, tk, tv = t(x["q"]), t(x["k"]), t(x["v"])
+        o = torch.empty_like(tq)
+        lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
+        pairs = allowed_pairs(w.l_q, w.l_k, True, w.win_l, w.win_r)
+        return (lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True, w.win_l,
+                                   w.win_r), fwd_flops(w.n, w.h, w.d, pairs),
+                "sliding-window forward")
+    if name.startswith("c5"):
+        w = WORKLOADS["C5"]
+        x = make_inputs(w)
+        tq, tk, tv = t(x["q"]), t(x["k"]), t(x["v"])
+        o = torch.empty_like(tq)
+        lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
+        pairs = allowed_pairs(w.l_q, w.l_k, True)
+        if name == "c5-fwd":
+            return (lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True),
+                    fwd_flops(w.n, w.h, w.d, pairs), "16k-token causal forward")
+        tdo = t(x["do"])
+        A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True)
+        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        ws = torch.empty(A.bwd_workspace_bytes(w.n, w.l_q, w.l_k, w.h, w.h_kv, w.d),
+                         dtype=torch.uint8, device=dev)
+        return (lambda: A.attn_bwd(tdo, tq, tk, tv, o, lse, dq, dk, dv, w.softmax_scale,
+                                   True, workspace=ws), bwd_flops(w.n, w.h, w.d, pairs),
+                "16k-token causal backward")
+    raise ValueError(f"unknown workload {name}")
+
+
 def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
            WORKLOADS, make_inputs):
+    """Every other targeted figure, each timed on its own: the rank-7 ring
+    share (per-chunk forwards, fused steps, one launch, all-gathered keys,
+    backward), the sliding window, the 16k-token forward and backward, and
+    the merge's bandwidth warm and cold."""
     dev = torch.device("cuda:0")
     res = {}
     steps = max(10, args.steps // 4)
+    t = lambda a: _dev_bf16(torch, a)
 
-    def t(xs):
-        return torch.from_numpy(xs).to(torch.bfloat16).to(dev)
-
-    # ring share, rank 7 of 8, GQA 32/8
     w = WORKLOADS["C3"]
     x = make_inputs(w)
     tq = t(x["q"])
     kc = [t(c) for c in x["k_chunks"]]
     vc = [t(c) for c in x["v_chunks"]]
+    offs = x["k_offsets"]
     share = A.RingShare(tq, w.softmax_scale, True, x["q_offset"])
+    pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, 7168, ko) for ko in offs)
+    fl = fwd_flops(1, 32, 128, pairs)
     fwd_ms = []
-    merge_ms = []
     for s in range(8):
         def f(s=s):
             A.attn_fwd(tq, kc[s], vc[s], share.blk, share.lse_blk,
-                       w.softmax_scale, True, -1, -1, x["q_offset"],
-                       x["k_offsets"][s])
+                       w.softmax_scale, True, -1, -1, x["q_offset"], offs[s])
         fwd_ms.append(timed(f, steps, 5, torch))
     A.attn_acc_init(share.acc, share.lse_acc)
-    merge_ms.append(timed(lambda: A.attn_merge(share.acc, share.lse_acc,
-                                               share.blk, share.lse_blk),
-                          steps, 5, torch))
-    e2e = timed(lambda: share.run(kc, vc, x["k_offsets"]), steps, 3, torch)
-    e2e_fused = timed(lambda: share.run(kc, vc, x["k_offsets"], fused=True),
-                      steps, 3, torch)
-    graph = share.capture(kc, vc, x["k_offsets"], fused=True)
-    e2e_graph = timed(graph.replay, steps, 3, torch)
+    merge_ms = timed(lambda: A.attn_merge(share.acc, share.lse_acc, share.blk,
+                                          share.lse_blk), steps, 5, torch)
+    e2e = timed(lambda: share.run(kc, vc, offs), steps, 3, torch)
+    e2e_fused = timed(lambda: share.run(kc, vc, offs, fused=True), steps, 3, torch)
+    e2e_one = timed(lambda: share.run(kc, vc, offs, one_launch=True), steps, 3, torch)
     # the all-gather form of the same share: the 8 chunks side by side, one
     # attn_fwd with the share's absolute query offset
     kf, vf = t(x["k_full"]), t(x["v_full"])
@@ -424,73 +535,56 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
     ag_lse = torch.empty((1, 32, 1024), dtype=torch.float32, device=dev)
     ag_ms = timed(lambda: A.attn_fwd(tq, kf, vf, ag_out, ag_lse, w.softmax_scale, True,
                                      -1, -1, x["q_offset"], 0), steps, 3, torch)
-    pairs = sum(allowed_pairs(1024, 1024, True, -1, -1, 7168, 1024 * s)
-                for s in range(8))
-    fl = fwd_flops(1, 32, 128, pairs)
     # the ring backward share of the same rank (dO drawn like the inputs)
-    tdo = t(np.random.default_rng(77).standard_normal(x["q"].shape)
-            .astype(np.float32))
-    out, lse = share.run(kc, vc, x["k_offsets"], fused=True)
+    tdo = t(np.random.default_rng(77).standard_normal(x["q"].shape).astype(np.float32))
+    out, lse = share.run(kc, vc, offs, one_launch=True)
     bshare = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, w.softmax_scale,
                             True, x["q_offset"])
-    bwd_ms = timed(lambda: bshare.run(kc, vc, x["k_offsets"]),
-                   max(5, steps // 4), 2, torch)
-    bgraph = bshare.capture(kc, vc, x["k_offsets"])
-    bwd_graph_ms = timed(bgraph.replay, max(5, steps // 4), 2, torch)
+    bwd_ms = timed(lambda: bshare.run(kc, vc, offs), max(5, steps // 4), 2, torch)
     mb = merge_bytes(1, 1024, 32, 128, 2)
+    tf = lambda ms, f=fl: round(f / (ms * 1e-3) / 1e12, 2)
+    bfl = bwd_flops(1, 32, 128, pairs)
     res["ring_share_rank7"] = {
-        "fwd_tflops_sum_of_8": round(fl / (sum(fwd_ms) * 1e-3) / 1e12, 2),
+        "algorithmic_gflop": round(fl / 1e9, 3),
+        "step_kernel": A.fwd_kernel_name(1, 1024, 1024, 32, 8, 128, True,
+                                         q_offset=7168, k_offset=0),
         "fwd_ms_per_step": [round(v, 4) for v in fwd_ms],
-        "merge_ms": round(merge_ms[0], 4),
-        "merge_gbs_warm": round(mb / (merge_ms[0] * 1e-3) / 1e9, 1),
-        "end_to_end_ms": round(e2e, 4),
-        "end_to_end_fused_ms": round(e2e_fused, 4),
-        "fused_tflops": round(fl / (e2e_fused * 1e-3) / 1e12, 2),
-        "end_to_end_fused_graph_ms": round(e2e_graph, 4),
-        "all_gather_share_ms": round(ag_ms, 4),
-        "all_gather_share_tflops": round(fl / (ag_ms * 1e-3) / 1e12, 2),
+        "fwd_ms_sum_of_8": round(sum(fwd_ms), 4),
+        "fwd_tflops_sum_of_8": tf(sum(fwd_ms)),
+        "fwd_frac_sum_of_8": _frac(tf(sum(fwd_ms))),
+        "merge_ms": round(merge_ms, 4),
+        "merge_gbs_warm": round(mb / (merge_ms * 1e-3) / 1e9, 1),
+        "unfused_ms": round(e2e, 4),
+        "unfused_tflops": tf(e2e),
+        "fused_steps_ms": round(e2e_fused, 4),
+        "fused_steps_tflops": tf(e2e_fused),
+        "fused_steps_frac": _frac(tf(e2e_fused)),
+        "one_launch_kernel": "fwd_pipe_kernel (8 chunks)",
+        "one_launch_ms": round(e2e_one, 4),
+        "one_launch_tflops": tf(e2e_one),
+        "one_launch_frac": _frac(tf(e2e_one)),
+        "all_gather_ms": round(ag_ms, 4),
+        "all_gather_tflops": tf(ag_ms),
         "backward_share_ms": round(bwd_ms, 4),
-        "backward_share_graph_ms": round(bwd_graph_ms, 4),
-        "backward_share_tflops": round(bwd_flops(1, 32, 128, pairs)
-                                       / (bwd_ms * 1e-3) / 1e12, 2)}
-    del bgraph, graph, bshare, tdo, kf, vf, ag_out, ag_lse
-    del share, kc, vc, tq
+        "backward_share_tflops": tf(bwd_ms, bfl),
+        "backward_share_frac": _frac(tf(bwd_ms, bfl))}
+    del bshare, tdo, kf, vf, ag_out, ag_lse, share, kc, vc, tq
 
-    # sliding window
-    w = WORKLOADS["C4"]
-    x = make_inputs(w)
-    tq, tk, tv = t(x["q"]), t(x["k"]), t(x["v"])
-    o = torch.empty_like(tq)
-    lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
-    ms = timed(lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True,
-                                  w.win_l, w.win_r), steps, 5, torch)
-    pairs = allowed_pairs(w.l_q, w.l_k, True, w.win_l, w.win_r)
-    fl = fwd_flops(w.n, w.h, w.d, pairs)
-    res["window_256"] = {"ms": round(ms, 4),
-                         "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
-    del tq, tk, tv, o, lse
-
-    # long context fwd (+ bwd)
-    w = WORKLOADS["C5"]
-    x = make_inputs(w)
-    tq, tk, tv, tdo = t(x["q"]), t(x["k"]), t(x["v"]), t(x["do"])
-    o = torch.empty_like(tq)
-    lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
-    ms = timed(lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True),
-               max(5, steps // 4), 3, torch)
-    pairs = allowed_pairs(w.l_q, w.l_k, True)
-    res["long_16k"] = {"fwd_ms": round(ms, 4),
-                       "fwd_tflops": round(fwd_flops(w.n, w.h, w.d, pairs)
-                                           / (ms * 1e-3) / 1e12, 2)}
-    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
-    ws = torch.empty(A.bwd_workspace_bytes(w.n, w.l_q, w.l_k, w.h, w.h_kv, w.d),
-                     dtype=torch.uint8, device=dev)
-    msb = timed(lambda: A.attn_bwd(tdo, tq, tk, tv, o, lse, dq, dk, dv,
-                                   w.softmax_scale, True, workspace=ws),
-                max(5, steps // 8), 2, torch)
-    res["long_16k"]["bwd_ms"] = round(msb, 4)
-    res["long_16k"]["bwd_tflops"] = round(
-        bwd_flops(w.n, w.h, w.d, pairs) / (msb * 1e-3) / 1e12, 2)
+    for key, name in (("window_256", "c4"), ("long_16k_fwd", "c5-fwd"),
+                      ("long_16k_bwd", "c5-bwd")):
+        fn, flops, what = single_workload(name, A, torch, allowed_pairs, fwd_flops,
+                                          bwd_flops, WORKLOADS, make_inputs)
+        n_steps = steps if name == "c4" else max(5, steps // 8)
+        ms = timed(fn, n_steps, 3, torch)
+        r = {"what": what, "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+             "frac": _frac(flops / (ms * 1e-3) / 1e12)}
+        if name == "c4":
+            r["kernel"] = A.fwd_kernel_name(4, 4096, 4096, 16, 16, 64, True, 256, 0)
+        if name == "c5-fwd":
+            r["kernel"] = A.fwd_kernel_name(1, 16384, 16384, 16, 16, 128, True)
+        res[key] = r
+        del fn
+        torch.cuda.empty_cache()
     res["merge"] = merge_measurements(A, torch, merge_bytes, steps)
     return res
 

@@ -39,6 +39,7 @@ SIGNATURES = {
     "attn_fwd_kernel_name": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _ll,
                                                _ll, _i, _i]),
     "attn_merge": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "attn_hbm_copy": (_i, [_vp, _vp, _ll, _vp]),
     "attn_acc_init": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_acc_cast": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,

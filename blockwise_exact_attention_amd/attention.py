@@ -177,6 +177,18 @@ def attn_fwd_ring(q, k_chunks, v_chunks, k_offsets, out, lse, scale, causal=Fals
     return out, lse
 
 
+def hbm_copy(src, dst, stream=None):
+    """The library's plain streaming copy (bandwidth reference) of src's bytes
+    into dst (same byte size, a multiple of 16)."""
+    _dev(src, dst)
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must have the same byte size")
+    check("attn_hbm_copy", _lib.lib().attn_hbm_copy(src.data_ptr(), dst.data_ptr(), nb,
+                                                      _stream(stream)))
+    return dst
+
+
 def attn_acc_init(out_acc, lse_acc=None, stream=None):
     """O = 0 and (unless lse_acc is None) LSE = -inf."""
     _dev(out_acc, *([] if lse_acc is None else [lse_acc]))

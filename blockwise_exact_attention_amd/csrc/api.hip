@@ -276,6 +276,16 @@ int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
                                   static_cast<hipStream_t>(stream)));
 }
 
+int attn_hbm_copy(const void* src, void* dst, long long bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || bytes > (1LL << 40)) return ATTN_ERR_SHAPE;
+  if (missing(src, bytes) || missing(dst, bytes)) return ATTN_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return ATTN_ERR_ALIGN;
+  if (overlap(range(src, bytes), range(dst, bytes))) return ATTN_ERR_ALIAS;
+  if (bytes == 0) return ATTN_OK;
+  (void)hipGetLastError();
+  return finish(bea::launch_hbm_copy(src, dst, bytes / 16, static_cast<hipStream_t>(stream)));
+}
+
 int attn_acc_init(float* out_acc, float* lse_acc, int n, int l, int h, int d,
                   void* stream) {
   if (!sizes_ok(n, l, h, d)) return ATTN_ERR_SHAPE;

@@ -54,6 +54,8 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
 hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
                         const float* lse_blk, int n, int l, int h, int d,
                         bool blk_bf16, hipStream_t stream);
+// n4 16-byte words from src to dst (the bandwidth reference of the merge).
+hipError_t launch_hbm_copy(const void* src, void* dst, long long n4, hipStream_t stream);
 // The merge of an all-empty block: accumulator rows whose LSE is -inf get
 // O = 0, the others are left alone.
 hipError_t launch_acc_clear_empty(float* out_acc, const float* lse_acc, int n, int l,

@@ -61,7 +61,9 @@ __device__ __forceinline__ void merge_row_weights(float* __restrict__ lse_acc,
 // reads are contiguous; its O rows are R rows h*d apart, each row contiguous.
 // Every thread issues its data loads (the block's values and, speculatively,
 // the accumulator's) before the row weights are known, so a block pays one
-// memory round trip, not two.
+// memory round trip, not two.  The O data is touched once per merge: its
+// loads and stores carry the nontemporal hint (streamed past the caches;
+// measured on gfx950 from HBM: 11.3 -> 9.6 us for a 42 MB merge).
 template <bool BLK_BF16>
 __global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
     float* __restrict__ acc, float* __restrict__ lse_acc,
@@ -95,13 +97,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
     if (rr < nr) {
       const size_t off = base + (size_t)rr * row_stride + (e - rr * d);
       if (BLK_BF16) {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(
-            static_cast<const uint16_t*>(blk) + off);
+        const u32x2_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(
+            static_cast<const uint16_t*>(blk) + off));
         bv[v] = f32x4_t{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
       } else {
-        bv[v] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(blk) + off);
+        bv[v] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t*>(static_cast<const float*>(blk) + off));
       }
-      av[v] = *reinterpret_cast<const f32x4_t*>(acc + off);
+      av[v] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(acc + off));
     }
   }
   if (tid < nr) {
@@ -137,12 +140,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
     // a row whose accumulator LSE is -inf takes the block as is, or zeros
     // when the block row is empty too (select, never a multiply, so
     // whatever the accumulator held cannot leak)
+    f32x4_t* dst = reinterpret_cast<f32x4_t*>(acc + off);
     if (mode == 1)
-      *reinterpret_cast<f32x4_t*>(acc + off) = bv[v];
+      __builtin_nontemporal_store(bv[v], dst);
     else if (mode == 3)
-      *reinterpret_cast<f32x4_t*>(acc + off) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      __builtin_nontemporal_store(f32x4_t{0.f, 0.f, 0.f, 0.f}, dst);
     else if (mode == 2)
-      *reinterpret_cast<f32x4_t*>(acc + off) = av[v] * s_wa[rr] + bv[v] * s_wb[rr];
+      __builtin_nontemporal_store(av[v] * s_wa[rr] + bv[v] * s_wb[rr], dst);
   }
 }
 
@@ -256,6 +260,16 @@ __global__ __launch_bounds__(256) void acc_cast_kernel(const float* __restrict__
   }
 }
 
+// A plain read-and-write stream of n4 16-byte words (nontemporal loads and
+// stores, one word per thread): what an elementwise kernel's HBM traffic can
+// reach on this GPU, the reference the merge is measured against.
+__global__ __launch_bounds__(256) void hbm_copy_kernel(const f32x4_t* __restrict__ src,
+                                                       f32x4_t* __restrict__ dst,
+                                                       long long n4) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(src + e), dst + e);
+}
+
 unsigned grid_for(long long work, int per_block) {
   long long g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -293,6 +307,12 @@ hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
   else
     hipLaunchKernelGGL((merge_kernel<false>), grid, block, 0, stream, out_acc,
                        lse_acc, out_blk, lse_blk, l, h, d, rows, rpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_hbm_copy(const void* src, void* dst, long long n4, hipStream_t stream) {
+  hipLaunchKernelGGL(hbm_copy_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const f32x4_t*>(src), static_cast<f32x4_t*>(dst), n4);
   return hipGetLastError();
 }
 

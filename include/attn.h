@@ -200,6 +200,14 @@ int attn_fwd_ring(const void* q, const void* const* k_chunks, const void* const*
                   void* stream, int dtype);
 
 /*
+ * attn_hbm_copy - a plain device copy of `bytes` bytes (a multiple of 16)
+ * by 16-byte nontemporal loads and stores: what a streaming elementwise
+ * kernel reaches on this GPU, the bandwidth reference the merge is measured
+ * against.  Not part of the attention path.  src and dst must not overlap.
+ */
+int attn_hbm_copy(const void* src, void* dst, long long bytes, void* stream);
+
+/*
  * attn_acc_init - set a ring accumulator to the empty result, O = 0 and
  * LSE = -inf (flash_sharding.py ring_fwd, its initial o and lse).
  *   out_acc [n,l,h,d] float32 out; lse_acc [n,h,l] float32 out, or NULL to

@@ -455,3 +455,13 @@ def test_fwd_kernel_name_reports_the_dispatch():
     assert fwd_kernel_name(1, 0, 128, 2, 2, 64) is None
     assert fwd_kernel_name(1, 128, 0, 2, 2, 64) is None
     assert fwd_kernel_name(1, 128, 128, 2, 2, 96) is None
+
+
+def test_hbm_copy_checks():
+    L = _lib.lib()
+    assert L.attn_hbm_copy(A, B, 100, None) == ATTN_ERR_SHAPE      # not a multiple of 16
+    assert L.attn_hbm_copy(A, B, -16, None) == ATTN_ERR_SHAPE
+    assert L.attn_hbm_copy(None, B, 64, None) == ATTN_ERR_NULL
+    assert L.attn_hbm_copy(A + 8, B, 64, None) == ATTN_ERR_ALIGN
+    assert L.attn_hbm_copy(A, A + 32, 64, None) == ATTN_ERR_ALIAS
+    assert L.attn_hbm_copy(None, None, 0, None) == ATTN_OK

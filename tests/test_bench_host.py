@@ -22,21 +22,25 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_counted_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
-    """Bytes are reported only from a counter summary whose recorded sha256
-    equals that of the forward kernel's current sources."""
+    """Bytes are reported only from a counter summary of the same kernel whose
+    recorded sha256 equals that of the kernel's current sources."""
     os.symlink(os.path.join(ROOT, "blockwise_exact_attention_amd"),
                tmp_path / "blockwise_exact_attention_amd")
     (tmp_path / "profiles").mkdir()
-    path = tmp_path / "profiles" / "fwd_bf16_causal_mha_n2_l2048_h16_d128_counters.json"
+    path = tmp_path / "profiles" / bench.COUNTERS_JSON
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.counted_traffic() is None          # no summary at all
-    sha = bench.kernel_sources_sha256()
-    path.write_text(json.dumps({"kernel_sources_sha256": sha,
+    kern = "fwd_bf16_kernel<128, 64, 2, false>"
+    assert bench.counted_traffic(kern) is None          # no summary at all
+    sha = bench.kernel_sources_sha256(kern)
+    path.write_text(json.dumps({"kernel": kern, "kernel_sources_sha256": sha,
                                 "hbm_bytes_per_launch": 12345}))
-    assert bench.counted_traffic() == 12345
-    path.write_text(json.dumps({"kernel_sources_sha256": "0" * 64,
+    assert bench.counted_traffic(kern) == 12345
+    # another kernel, or the other kernel file's sources
+    assert bench.counted_traffic("fwd_bf16_kernel<128, 64, 1, false>") is None
+    assert bench.kernel_sources_sha256("fwd_pipe_kernel<128, 2, false, false>") != sha
+    path.write_text(json.dumps({"kernel": kern, "kernel_sources_sha256": "0" * 64,
                                 "hbm_bytes_per_launch": 12345}))
-    assert bench.counted_traffic() is None
+    assert bench.counted_traffic(kern) is None
 
 
 def test_workload_counts():

@@ -124,3 +124,14 @@ def test_backward_without_keys_or_rows():
     torch.cuda.synchronize()
     for t in acc + acc2:
         assert bool((t == 2.5).all())
+
+
+def test_hbm_copy_reference_copies():
+    """The bandwidth reference of the merge is a plain copy: dst equals src
+    bit for bit, and nothing past dst's end is touched."""
+    src = torch.randn(3 * 4096 + 4, device="cuda")
+    buf = torch.full((3 * 4096 + 4 + 64,), 7.0, device="cuda")
+    A.hbm_copy(src, buf[:src.numel()])
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:src.numel()], src)
+    assert torch.all(buf[src.numel():] == 7.0)
