@@ -111,9 +111,9 @@ def cpu_baseline(x, w, seconds):
 
 
 def kernel_sources(kernel):
-    """The source files a forward kernel is built from."""
+    """The source files that define a forward kernel's code."""
     main = "fwd_pipe.hip" if kernel.startswith("fwd_pipe") else "fwd.hip"
-    return (main, "tile.hpp", "common.hpp", "launch.hpp")
+    return (main, "tile.hpp", "common.hpp")
 
 
 def kernel_sources_sha256(kernel):

@@ -277,27 +277,50 @@ def attn_bwd(dout, q, k, v, out, lse, dq, dk, dv, scale, causal=False,
     return dq, dk, dv
 
 
+def attn_bwd_prepare(dout, out, lse, workspace, stream=None):
+    """D = rowsum(dout * out) and the LSE in base-2 units of the query rows,
+    into the leading bwd_prepare_bytes(...) bytes of `workspace` (a uint8
+    device tensor), for attn_bwd_acc(..., prepared=True)."""
+    if dout.dim() != 4 or out.shape != dout.shape or out.dtype != dout.dtype:
+        raise ValueError("dout and out must be [n, l_q, h, d] of one dtype")
+    n, l_q, h, d = dout.shape
+    if tuple(lse.shape) != (n, h, l_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [n, h, l_q]")
+    _dev(dout, out, lse, workspace)
+    st = _lib.lib().attn_bwd_prepare(dout.data_ptr(), out.data_ptr(), lse.data_ptr(), n,
+                                     l_q, h, d, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream), _dtype_code(dout))
+    check("attn_bwd_prepare", st)
+    return workspace
+
+
+def bwd_prepare_bytes(n, l_q, h):
+    return int(_lib.lib().attn_bwd_prepare_bytes(n, l_q, h))
+
+
 def attn_bwd_acc(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, scale,
                  causal=False, win_l=-1, win_r=-1, q_offset=0, k_offset=0,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, prepared=False):
     """One ring backward step: this chunk's gradients added to the float32
     accumulators dq_acc (shaped like q), dk_acc and dv_acc (shaped like k);
-    out and lse are the query rows' results over the whole sequence."""
+    out and lse are the query rows' results over the whole sequence.
+    prepared=True: `workspace` already holds what attn_bwd_prepare wrote for
+    these dout, out and lse (attn_bwd_acc_prepared, no preprocessing)."""
+    if prepared and workspace is None:
+        raise ValueError("prepared=True needs the prepared workspace")
     _check_bwd(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, acc=True)
     n, l_q, h, d = q.shape
     _, l_k, h_kv, _ = k.shape
     need = bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d)
     workspace = _workspace(workspace, need, q.device, stream)
-    st = _lib.lib().attn_bwd_acc(dout.data_ptr(), q.data_ptr(), k.data_ptr(),
-                                 v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                 dq_acc.data_ptr(), dk_acc.data_ptr(),
-                                 dv_acc.data_ptr(), n, l_q, l_k, h, h_kv, d,
-                                 float(scale), int(bool(causal)), int(win_l),
-                                 int(win_r), int(q_offset), int(k_offset),
-                                 workspace.data_ptr(),
-                                 workspace.numel() * workspace.element_size(),
-                                 _stream(stream), _dtype_code(q))
-    check("attn_bwd_acc", st)
+    fn = _lib.lib().attn_bwd_acc_prepared if prepared else _lib.lib().attn_bwd_acc
+    st = fn(dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), dq_acc.data_ptr(), dk_acc.data_ptr(), dv_acc.data_ptr(), n, l_q,
+            l_k, h, h_kv, d, float(scale), int(bool(causal)), int(win_l), int(win_r),
+            int(q_offset), int(k_offset), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(stream), _dtype_code(q))
+    check("attn_bwd_acc_prepared" if prepared else "attn_bwd_acc", st)
     return dq_acc, dk_acc, dv_acc
 
 
@@ -448,8 +471,9 @@ def ring_share(q, k_chunks, v_chunks, k_offsets, q_offset, scale=None,
 class RingShareBwd:
     """One device's share of the ring backward (picotron
     ring_attention_backward): given its query block q with the forward ring
-    share's final (out, lse) and the incoming gradient dout, `run` adds every
-    key/value chunk's contribution with attn_bwd_acc - dQ accumulating
+    share's final (out, lse) and the incoming gradient dout, `run` prepares
+    the per-row D and LSE once (attn_bwd_prepare), adds every key/value
+    chunk's contribution with attn_bwd_acc_prepared - dQ accumulating
     locally in float32, one float32 (dK, dV) accumulator per chunk (in a real
     ring those travel with the chunk) - and casts dQ to q's dtype at the end.
     Buffers are allocated once; everything runs on one stream."""
@@ -481,19 +505,20 @@ class RingShareBwd:
                            for s in range(P)]
             self.dv_acc = [self.kv_acc[(P + s) * shape[0]:(P + s + 1) * shape[0]]
                            for s in range(P)]
-        if self.ws is None:
-            _, l_k, h_kv, _ = shape
-            need = bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d)
-            self.ws = torch.empty(max(need, 1), dtype=torch.uint8,
-                                  device=self.q.device)
+        need = max([bwd_workspace_bytes(n, l_q, c.shape[1], h, c.shape[2], d)
+                    for c in k_chunks] + [bwd_prepare_bytes(n, l_q, h), 1])
+        if self.ws is None or self.ws.numel() < need:
+            with _on(stream):
+                self.ws = torch.empty(need, dtype=torch.uint8, device=self.q.device)
         attn_acc_init(self.dq_acc, None, stream)
         attn_acc_init(self.kv_acc, None, stream)
+        attn_bwd_prepare(self.dout, self.out, self.lse, self.ws, stream)
         for kc, vc, ko, dka, dva in zip(k_chunks, v_chunks, k_offsets,
                                         self.dk_acc, self.dv_acc):
             attn_bwd_acc(self.dout, self.q, kc, vc, self.out, self.lse,
                          self.dq_acc, dka, dva, self.scale, self.causal,
                          self.window[0], self.window[1], self.q_offset, ko,
-                         self.ws, stream)
+                         self.ws, stream, prepared=True)
         attn_acc_cast(self.dq_acc, self.dq, stream)
         return self.dq, self.dk_acc, self.dv_acc
 

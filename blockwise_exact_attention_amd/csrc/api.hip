@@ -376,7 +376,8 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
               int n, int l_q, int l_k, int h, int h_kv, int d, float scale,
               int causal, int win_l, int win_r, long long q_offset,
               long long k_offset, void* workspace, size_t workspace_bytes,
-              void* stream, int dtype, bool acc, bool use_scratch = false) {
+              void* stream, int dtype, bool acc, bool use_scratch = false,
+              bool prepared = false) {
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
@@ -439,7 +440,7 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
   if (acc)
     return finish(bea::launch_bwd(dout, q, k, v, out, lse, nullptr, nullptr, nullptr,
                                   s, workspace, true, hs, static_cast<float*>(dq),
-                                  static_cast<float*>(dk), static_cast<float*>(dv)));
+                                  static_cast<float*>(dk), static_cast<float*>(dv), prepared));
   return finish(bea::launch_bwd(dout, q, k, v, out, lse, dq, dk, dv, s, workspace,
                                 true, hs));
 }
@@ -468,6 +469,47 @@ int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
   return bwd_entry(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, n, l_q, l_k, h,
                    h_kv, d, scale, causal, win_l, win_r, q_offset, k_offset,
                    workspace, workspace_bytes, stream, dtype, true);
+}
+
+size_t attn_bwd_prepare_bytes(int n, int l_q, int h) {
+  if (!sizes_ok(n, l_q, h, 64)) return 0;
+  if ((long long)n * l_q == 0) return 0;
+  return bea::bwd_prepared_bytes(n, l_q, h);
+}
+
+int attn_bwd_prepare(const void* dout, const void* out, const float* lse, int n, int l_q,
+                     int h, int d, void* workspace, size_t workspace_bytes, void* stream,
+                     int dtype) {
+  // the query-side checks of the backward, with one key/value head
+  int st = check_attn_args(n, l_q, 0, h, 1, d, 0.f, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const long long qe = (long long)n * l_q * h * d;
+  const long long lb = (long long)n * h * l_q * 4;
+  if (missing(dout, qe) || missing(out, qe) || missing(lse, lb)) return ATTN_ERR_NULL;
+  if (qe == 0) return ATTN_OK;
+  const size_t need = bea::bwd_prepared_bytes(n, l_q, h);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned(dout, 16) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
+    return ATTN_ERR_ALIGN;
+  const Range rw = range(workspace, (long long)need);
+  if (overlap(rw, range(dout, qe * 2)) || overlap(rw, range(out, qe * 2)) ||
+      overlap(rw, range(lse, lb)))
+    return ATTN_ERR_ALIAS;
+  (void)hipGetLastError();
+  return finish(bea::launch_bwd_prepare(dout, out, lse, n, l_q, h, d, workspace,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_acc_prepared(const void* dout, const void* q, const void* k, const void* v,
+                          const void* out, const float* lse, float* dq_acc, float* dk_acc,
+                          float* dv_acc, int n, int l_q, int l_k, int h, int h_kv, int d,
+                          float scale, int causal, int win_l, int win_r, long long q_offset,
+                          long long k_offset, void* workspace, size_t workspace_bytes,
+                          void* stream, int dtype) {
+  return bwd_entry(dout, q, k, v, out, lse, dq_acc, dk_acc, dv_acc, n, l_q, l_k, h, h_kv, d,
+                   scale, causal, win_l, win_r, q_offset, k_offset, workspace,
+                   workspace_bytes, stream, dtype, true, false, true);
 }
 
 int attn_bwd_static(const void* dout, const void* q, const void* k, const void* v,

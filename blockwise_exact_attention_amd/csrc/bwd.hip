@@ -805,12 +805,17 @@ BwdWorkspace bwd_layout(int n, int l_q, int l_k, int h, int h_kv, int d) {
   return w;
 }
 
-template <int D, bool ACC>
-hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream) {
+template <int D>
+void launch_pre_d(const BwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.n * p.l_q * p.h;
   const long long pre_blocks = (rows * (D / 8) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(kThreads),
                      0, stream, p);
+}
+
+template <int D, bool ACC>
+hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream, bool prepared) {
+  if (!prepared) launch_pre_d<D>(p, stream);
   const int n_ktiles = (p.l_k + kKeysPerWG - 1) / kKeysPerWG;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, ACC>),
                      dim3((unsigned)(p.split * n_ktiles * p.n * p.h_kv)), dim3(kThreads),
@@ -840,11 +845,34 @@ size_t bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d) {
   return bwd_layout(n, l_q, l_k, h, h_kv, d).total;
 }
 
+size_t bwd_prepared_bytes(int n, int l_q, int h) {
+  // D and LSE2 come first in every layout, whatever the key count
+  return bwd_layout(n, l_q, 1, h, 1, 64).part;
+}
+
+hipError_t launch_bwd_prepare(const void* dout, const void* out, const float* lse, int n,
+                              int l_q, int h, int d, void* workspace, hipStream_t stream) {
+  BwdParams p{};
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.o = static_cast<const uint16_t*>(out);
+  p.lse = lse;
+  const BwdWorkspace w = bwd_layout(n, l_q, 1, h, 1, d);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  p.dd = reinterpret_cast<float*>(ws + w.dd);
+  p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
+  p.n = n;
+  p.l_q = l_q;
+  p.h = h;
+  if (d == 128) launch_pre_d<128>(p, stream);
+  else launch_pre_d<64>(p, stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd(const void* dout, const void* q, const void* k,
                       const void* v, const void* out, const float* lse,
                       void* dq, void* dk, void* dv, const AttnShape& s,
                       void* workspace, bool bf16, hipStream_t stream,
-                      float* dq_acc, float* dk_acc, float* dv_acc) {
+                      float* dq_acc, float* dk_acc, float* dv_acc, bool prepared) {
   if (!bf16) return hipErrorNotSupported;
   BwdParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -878,10 +906,10 @@ hipError_t launch_bwd(const void* dout, const void* q, const void* k,
   p.dlo = s.dlo;
   p.dhi = s.dhi;
   if (dq_acc != nullptr)
-    return s.d == 128 ? launch_bwd_d<128, true>(p, s.causal, stream)
-                      : launch_bwd_d<64, true>(p, s.causal, stream);
-  return s.d == 128 ? launch_bwd_d<128, false>(p, s.causal, stream)
-                    : launch_bwd_d<64, false>(p, s.causal, stream);
+    return s.d == 128 ? launch_bwd_d<128, true>(p, s.causal, stream, prepared)
+                      : launch_bwd_d<64, true>(p, s.causal, stream, prepared);
+  return s.d == 128 ? launch_bwd_d<128, false>(p, s.causal, stream, prepared)
+                    : launch_bwd_d<64, false>(p, s.causal, stream, prepared);
 }
 
 }  // namespace bea

@@ -66,13 +66,21 @@ hipError_t launch_acc_cast(const float* out_acc, void* out, int n, int l,
                            int h, int d, bool bf16, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);
+// Leading bytes of every backward workspace that hold the per-row D and
+// LSE * log2(e).
+size_t bwd_prepared_bytes(int n, int l_q, int h);
+// Writes those rows (D = rowsum(dout * out), LSE in log2 units) into the
+// workspace.
+hipError_t launch_bwd_prepare(const void* dout, const void* out, const float* lse, int n,
+                              int l_q, int h, int d, void* workspace, hipStream_t stream);
 // dq_acc != nullptr: add the gradients to the fp32 accumulators (dq_acc,
-// dk_acc, dv_acc) instead of writing dq, dk, dv.
+// dk_acc, dv_acc) instead of writing dq, dk, dv.  prepared: the workspace
+// already holds the rows launch_bwd_prepare writes (not recomputed).
 hipError_t launch_bwd(const void* dout, const void* q, const void* k,
                       const void* v, const void* out, const float* lse,
                       void* dq, void* dk, void* dv, const AttnShape& s,
                       void* workspace, bool bf16, hipStream_t stream,
                       float* dq_acc = nullptr, float* dk_acc = nullptr,
-                      float* dv_acc = nullptr);
+                      float* dv_acc = nullptr, bool prepared = false);
 
 }  // namespace bea

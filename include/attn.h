@@ -282,6 +282,36 @@ int attn_bwd_acc(const void* dout, const void* q, const void* k, const void* v,
 size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);
 
 /*
+ * attn_bwd_prepare + attn_bwd_acc_prepared - the ring backward share with
+ * its per-row preprocessing done once (picotron ring_attention_backward
+ * forms D = rowsum(dO * O) from the saved global output once, before the
+ * loop over the chunks; flash_sharding.py ring_bwd likewise passes the same
+ * (o, lse, do) to every chunk's backward).
+ *
+ * attn_bwd_prepare writes, for the query rows of (dout, out, lse), D and the
+ * LSE in base-2 units into the first attn_bwd_prepare_bytes(n, l_q, h)
+ * bytes of `workspace` (at least that many; 16-byte aligned).  Shapes as
+ * for attn_bwd; dtype must be ATTN_BF16.
+ *
+ * attn_bwd_acc_prepared is attn_bwd_acc (same arguments and workspace
+ * size) without that preprocessing: it reads D and the LSE from the
+ * workspace, which must hold what attn_bwd_prepare wrote for the same
+ * dout, out, lse and sizes, untouched since (the calls in between may be
+ * other attn_bwd_acc_prepared calls of the share, which only write the
+ * rest of the workspace).  Results equal attn_bwd_acc's bit for bit.
+ */
+size_t attn_bwd_prepare_bytes(int n, int l_q, int h);
+int attn_bwd_prepare(const void* dout, const void* out, const float* lse, int n, int l_q,
+                     int h, int d, void* workspace, size_t workspace_bytes, void* stream,
+                     int dtype);
+int attn_bwd_acc_prepared(const void* dout, const void* q, const void* k, const void* v,
+                          const void* out, const float* lse, float* dq_acc, float* dk_acc,
+                          float* dv_acc, int n, int l_q, int l_k, int h, int h_kv, int d,
+                          float scale, int causal, int win_l, int win_r, long long q_offset,
+                          long long k_offset, void* workspace, size_t workspace_bytes,
+                          void* stream, int dtype);
+
+/*
  * attn_bwd_static - attn_bwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same computation and results, with the workspace taken

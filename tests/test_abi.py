@@ -465,3 +465,42 @@ def test_hbm_copy_checks():
     assert L.attn_hbm_copy(A + 8, B, 64, None) == ATTN_ERR_ALIGN
     assert L.attn_hbm_copy(A, A + 32, 64, None) == ATTN_ERR_ALIAS
     assert L.attn_hbm_copy(None, None, 0, None) == ATTN_OK
+
+
+def test_bwd_prepare_checks():
+    """The once-per-share preprocessing and the prepared step check their
+    arguments before any HIP call (fake addresses)."""
+    L = _lib.lib()
+    need = L.attn_bwd_prepare_bytes(1, 128, 2)
+    assert need >= 2 * 128 * 2 * 4
+    assert L.attn_bwd_prepare_bytes(1, 0, 2) == 0
+    assert L.attn_bwd_prepare_bytes(-1, 128, 2) == 0
+
+    def prep(dout=A, out=B, lse=C, ws=D_, wsb=need, d=64, h=2, dtype=ATTN_BF16, l_q=128):
+        return L.attn_bwd_prepare(dout, out, lse, 1, l_q, h, d, ws, wsb, None, dtype)
+    assert prep(dout=None) == ATTN_ERR_NULL
+    assert prep(lse=None) == ATTN_ERR_NULL
+    assert prep(d=96) == ATTN_ERR_UNSUPPORTED
+    assert prep(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    assert prep(l_q=-1) == ATTN_ERR_SHAPE
+    assert prep(ws=None) == ATTN_ERR_WORKSPACE
+    assert prep(wsb=need - 1) == ATTN_ERR_WORKSPACE
+    assert prep(out=B + 8) == ATTN_ERR_ALIGN
+    assert prep(ws=A + 256) == ATTN_ERR_ALIAS
+    assert prep(l_q=0, dout=None, out=None, lse=None, ws=None) == ATTN_OK
+
+    ptrs = [A, A + (1 << 28), B, B + (1 << 28), C, C + (1 << 28), D_,
+            D_ + (1 << 28), E]
+    wneed = L.attn_bwd_workspace_bytes(1, 128, 128, 2, 2, 64)
+
+    def step(ptrs=ptrs, ws=F, wsb=wneed, h=2, dtype=ATTN_BF16):
+        return L.attn_bwd_acc_prepared(*ptrs, 1, 128, 128, h, 2, 64, 0.125, 1, -1, -1, 0, 0,
+                                       ws, wsb, None, dtype)
+    bad = list(ptrs)
+    bad[2] = None
+    assert step(ptrs=bad) == ATTN_ERR_NULL
+    assert step(h=3) == ATTN_ERR_SHAPE
+    assert step(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    assert step(ws=None) == ATTN_ERR_WORKSPACE
+    assert step(wsb=wneed - 1) == ATTN_ERR_WORKSPACE
+    assert step(ws=ptrs[7]) == ATTN_ERR_ALIAS

@@ -181,6 +181,42 @@ def test_ring_share_backward(d, h_kv, window, fused):
                        f"rank {r} chunk {s} dv")
 
 
+def test_prepared_ring_steps_equal_unprepared():
+    """The share's backward with D and the LSE prepared once
+    (attn_bwd_prepare + attn_bwd_acc_prepared, as RingShareBwd runs it)
+    equals per-chunk attn_bwd_acc, which prepares them itself, bit for bit;
+    and a second run on the same share object gives the same again."""
+    P, c, h, h_kv, d = 3, 200, 8, 2, 128
+    L = P * c
+    q, k, v, do = (round_to_bf16(x) for x in draw_normal(
+        57, [(1, L, h, d), (1, L, h_kv, d), (1, L, h_kv, d), (1, L, h, d)]))
+    scale = 1.0 / math.sqrt(d)
+    kc = [dev(k[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
+    vc = [dev(v[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
+    offs = [s * c for s in range(P)]
+    r = P - 1
+    tq, tdo = dev(q[:, r * c:], "bf16"), dev(do[:, r * c:], "bf16")
+    out, lse = A.ring_share(tq, kc, vc, offs, r * c, scale, True, one_launch=True)
+    out, lse = out.clone(), lse.clone()
+    share = A.RingShareBwd(tq, out, lse, tdo, scale, True, r * c)
+    dq1, dk1, dv1 = share.run(kc, vc, offs)
+    dq1, dk1, dv1 = dq1.clone(), [t.clone() for t in dk1], [t.clone() for t in dv1]
+    dq_acc = torch.zeros(tq.shape, dtype=torch.float32, device="cuda")
+    for s in range(P):
+        dka = torch.zeros(kc[s].shape, dtype=torch.float32, device="cuda")
+        dva = torch.zeros_like(dka)
+        A.attn_bwd_acc(tdo, tq, kc[s], vc[s], out, lse, dq_acc, dka, dva, scale, True,
+                       -1, -1, r * c, offs[s])
+        torch.cuda.synchronize()
+        assert torch.equal(dka, dk1[s]) and torch.equal(dva, dv1[s]), f"chunk {s}"
+    dq_ref = A.attn_acc_cast(dq_acc, torch.empty_like(tq))
+    torch.cuda.synchronize()
+    assert torch.equal(dq_ref, dq1)
+    dq2, dk2, dv2 = share.run(kc, vc, offs)
+    torch.cuda.synchronize()
+    assert torch.equal(dq2, dq1) and all(torch.equal(a, b) for a, b in zip(dk2, dk1))
+
+
 def test_c3_ring_share_backward():
     """The ring backward share of rank 7 at the ring workload's full size
     (1024 query rows, 8 chunks of 1024 keys, GQA 32/8), every key/value
