@@ -1,7 +1,7 @@
 """Benchmark of the blockwise exact-attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
-    python bench.py --workload {c3-steps,c3-fused,c3-share,c3-bwd,c4,c5-fwd,c5-bwd}
+    python bench.py --workload {c3-steps,c3-fused,c3-share,c3-bwd,c3-bwd-one,c4,c5-fwd,c5-bwd}
 
 Workload: causal multi-head attention, n=2, l=2048, h=h_kv=16, d=128, bf16,
 scale 1/sqrt(128), synthetic N(0,1) inputs resident in HBM.  A step is one
@@ -42,8 +42,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline workload (and the CPU baseline)")
     ap.add_argument("--workload", default="c2",
-                    choices=("c2", "c3-steps", "c3-fused", "c3-share", "c3-bwd", "c4",
-                             "c5-fwd", "c5-bwd"),
+                    choices=("c2", "c3-steps", "c3-fused", "c3-share", "c3-bwd", "c3-bwd-one",
+                             "c4", "c5-fwd", "c5-bwd"),
                     help="time only this workload's call (for profiler runs); c2 "
                          "is the default full run")
     ap.add_argument("--no-cpu", action="store_true")
@@ -458,13 +458,14 @@ def single_workload(name, A, torch, allowed_pairs, fwd_flops, bwd_flops, WORKLOA
         if name == "c3-share":
             return (lambda: share.run(kc, vc, offs, one_launch=True),
                     fwd_flops(1, 32, 128, pairs), "rank-7 share in one attn_fwd_ring launch")
-        if name == "c3-bwd":
+        if name in ("c3-bwd", "c3-bwd-one"):
             tdo = t(np.random.default_rng(77).standard_normal(x["q"].shape).astype(np.float32))
             o, l = share.run(kc, vc, offs, one_launch=True)
             b = A.RingShareBwd(tq, o.clone(), l.clone(), tdo, w.softmax_scale, True,
                                x["q_offset"])
-            return (lambda: b.run(kc, vc, offs), bwd_flops(1, 32, 128, pairs),
-                    "rank-7 ring backward share")
+            one = name == "c3-bwd-one"
+            return (lambda: b.run(kc, vc, offs, one_launch=one), bwd_flops(1, 32, 128, pairs),
+                    "rank-7 ring backward share" + (" in three launches" if one else ""))
     if name == "c4":
         w = WORKLOADS["C4"]
         x = make_inputs(w)
@@ -541,6 +542,8 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
     bshare = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, w.softmax_scale,
                             True, x["q_offset"])
     bwd_ms = timed(lambda: bshare.run(kc, vc, offs), max(5, steps // 4), 2, torch)
+    bwd_one_ms = timed(lambda: bshare.run(kc, vc, offs, one_launch=True), max(5, steps // 4),
+                       2, torch)
     mb = merge_bytes(1, 1024, 32, 128, 2)
     tf = lambda ms, f=fl: round(f / (ms * 1e-3) / 1e12, 2)
     bfl = bwd_flops(1, 32, 128, pairs)
@@ -567,7 +570,10 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
         "all_gather_tflops": tf(ag_ms),
         "backward_share_ms": round(bwd_ms, 4),
         "backward_share_tflops": tf(bwd_ms, bfl),
-        "backward_share_frac": _frac(tf(bwd_ms, bfl))}
+        "backward_share_frac": _frac(tf(bwd_ms, bfl)),
+        "backward_share_one_launch_ms": round(bwd_one_ms, 4),
+        "backward_share_one_launch_tflops": tf(bwd_one_ms, bfl),
+        "backward_share_one_launch_frac": _frac(tf(bwd_one_ms, bfl))}
     del bshare, tdo, kf, vf, ag_out, ag_lse, share, kc, vc, tq
 
     for key, name in (("window_256", "c4"), ("long_16k_fwd", "c5-fwd"),

@@ -51,6 +51,8 @@ SIGNATURES = {
     "attn_bwd_acc_prepared": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                    _i, _i, _i, _i, _f, _i, _i, _i, _ll, _ll, _vp, _sz,
                                    _vp, _i]),
+    "attn_bwd_ring": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i,
+                           _i, _i, _i, _f, _i, _i, _i, _ll, _vp, _sz, _vp, _i]),
     "attn_bwd_static": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
                              _i, _i, _i, _f, _i, _i, _i, _ll, _ll, _vp, _i]),
     "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),

@@ -295,6 +295,52 @@ def attn_bwd_prepare(dout, out, lse, workspace, stream=None):
     return workspace
 
 
+def attn_bwd_ring(dout, q, out, lse, k_chunks, v_chunks, k_offsets, dk_acc, dv_acc, dq,
+                  scale, causal=False, win_l=-1, win_r=-1, q_offset=0, workspace=None,
+                  stream=None):
+    """The whole ring backward share in three launches: dq (q's dtype) written
+    with the gradient over every chunk; chunk c's dK, dV added to the float32
+    accumulators dk_acc[c], dv_acc[c] (shaped like the chunk)."""
+    nc = len(k_chunks)
+    if not (len(v_chunks) == len(k_offsets) == len(dk_acc) == len(dv_acc) == nc):
+        raise ValueError("one entry per chunk in every list")
+    if not 1 <= nc <= _lib.ATTN_RING_MAX_CHUNKS:
+        raise ValueError(f"1 to {_lib.ATTN_RING_MAX_CHUNKS} chunks, got {nc}")
+    if q.dim() != 4:
+        raise ValueError("q must be [n, l_q, h, d]")
+    n, l_q, h, d = q.shape
+    h_kv = k_chunks[0].shape[2] if k_chunks[0].dim() == 4 else -1
+    for name, t in (("dout", dout), ("out", out), ("dq", dq)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    if tuple(lse.shape) != (n, h, l_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [n, h, l_q]")
+    for kc, vc, dka, dva in zip(k_chunks, v_chunks, dk_acc, dv_acc):
+        if kc.dim() != 4 or kc.shape != vc.shape or kc.shape[0] != n or \
+                kc.shape[2] != h_kv or kc.shape[3] != d:
+            raise ValueError("every k and v chunk must be [n, l_k, h_kv, d] matching q")
+        if kc.dtype != q.dtype or vc.dtype != q.dtype:
+            raise ValueError("q and the chunks must share a dtype")
+        if dka.shape != kc.shape or dva.shape != kc.shape or \
+                dka.dtype != torch.float32 or dva.dtype != torch.float32:
+            raise ValueError("dk_acc and dv_acc must be float32 shaped like their chunk")
+    _dev(dout, q, out, lse, dq, *k_chunks, *v_chunks, *dk_acc, *dv_acc)
+    need = bwd_prepare_bytes(n, l_q, h)
+    workspace = _workspace(workspace, need, q.device, stream)
+    arr = lambda ts: (ctypes.c_void_p * nc)(*[t.data_ptr() for t in ts])
+    lk = (ctypes.c_int * nc)(*[t.shape[1] for t in k_chunks])
+    ko = (ctypes.c_longlong * nc)(*[int(o) for o in k_offsets])
+    st = _lib.lib().attn_bwd_ring(dout.data_ptr(), q.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  arr(k_chunks), arr(v_chunks), lk, ko, arr(dk_acc),
+                                  arr(dv_acc), nc, dq.data_ptr(), n, l_q, h, h_kv, d,
+                                  float(scale), int(bool(causal)), int(win_l), int(win_r),
+                                  int(q_offset), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream(stream), _dtype_code(q))
+    check("attn_bwd_ring", st)
+    return dq, dk_acc, dv_acc
+
+
 def bwd_prepare_bytes(n, l_q, h):
     return int(_lib.lib().attn_bwd_prepare_bytes(n, l_q, h))
 
@@ -492,7 +538,10 @@ class RingShareBwd:
         self.dv_acc = []
         self.ws = None
 
-    def run(self, k_chunks, v_chunks, k_offsets, stream=None):
+    def run(self, k_chunks, v_chunks, k_offsets, stream=None, one_launch=False):
+        """one_launch=True: the share as attn_bwd_ring (prepare, one dK/dV
+        launch over all chunks, one dQ launch; at most ATTN_RING_MAX_CHUNKS
+        chunks) instead of a step per chunk."""
         n, l_q, h, d = self.q.shape
         P = len(k_chunks)
         shape = tuple(k_chunks[0].shape)
@@ -510,6 +559,13 @@ class RingShareBwd:
         if self.ws is None or self.ws.numel() < need:
             with _on(stream):
                 self.ws = torch.empty(need, dtype=torch.uint8, device=self.q.device)
+        if one_launch:
+            attn_acc_init(self.kv_acc, None, stream)
+            attn_bwd_ring(self.dout, self.q, self.out, self.lse, k_chunks, v_chunks,
+                          k_offsets, self.dk_acc, self.dv_acc, self.dq, self.scale,
+                          self.causal, self.window[0], self.window[1], self.q_offset,
+                          self.ws, stream)
+            return self.dq, self.dk_acc, self.dv_acc
         attn_acc_init(self.dq_acc, None, stream)
         attn_acc_init(self.kv_acc, None, stream)
         attn_bwd_prepare(self.dout, self.out, self.lse, self.ws, stream)

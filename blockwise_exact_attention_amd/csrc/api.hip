@@ -512,6 +512,87 @@ int attn_bwd_acc_prepared(const void* dout, const void* q, const void* k, const 
                    workspace_bytes, stream, dtype, true, false, true);
 }
 
+int attn_bwd_ring(const void* dout, const void* q, const void* out, const float* lse,
+                  const void* const* k_chunks, const void* const* v_chunks,
+                  const int* l_k_chunks, const long long* k_offsets,
+                  float* const* dk_acc_chunks, float* const* dv_acc_chunks, int n_chunks,
+                  void* dq, int n, int l_q, int h, int h_kv, int d, float scale, int causal,
+                  int win_l, int win_r, long long q_offset, void* workspace,
+                  size_t workspace_bytes, void* stream, int dtype) {
+  if (n_chunks < 1 || n_chunks > ATTN_RING_MAX_CHUNKS) return ATTN_ERR_SHAPE;
+  if (k_chunks == nullptr || v_chunks == nullptr || l_k_chunks == nullptr ||
+      k_offsets == nullptr || dk_acc_chunks == nullptr || dv_acc_chunks == nullptr)
+    return ATTN_ERR_NULL;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int st = check_attn_args(n, l_q, l_k_chunks[c], h, h_kv, d, scale, dtype);
+    if (st != ATTN_OK) return st;
+  }
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const long long qe = (long long)n * l_q * h * d;
+  const long long lb = (long long)n * h * l_q * 4;
+  if (missing(dout, qe) || missing(q, qe) || missing(out, qe) || missing(lse, lb) ||
+      missing(dq, qe))
+    return ATTN_ERR_NULL;
+  bool any_keys = false;
+  for (int c = 0; c < n_chunks; ++c) {
+    const long long ke = (long long)n * l_k_chunks[c] * h_kv * d;
+    if (missing(k_chunks[c], ke) || missing(v_chunks[c], ke) || missing(dk_acc_chunks[c], ke) ||
+        missing(dv_acc_chunks[c], ke))
+      return ATTN_ERR_NULL;
+    any_keys = any_keys || ke > 0;
+  }
+  const bool work = qe > 0 && any_keys;
+  const size_t need = work ? bea::bwd_prepared_bytes(n, l_q, h) : 0;
+  if (missing(workspace, (long long)need) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned(dout, 16) || !aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(dq, 16) || !aligned(workspace, 16))
+    return ATTN_ERR_ALIGN;
+  for (int c = 0; c < n_chunks; ++c)
+    if (!aligned(k_chunks[c], 16) || !aligned(v_chunks[c], 16) ||
+        !aligned(dk_acc_chunks[c], 16) || !aligned(dv_acc_chunks[c], 16))
+      return ATTN_ERR_ALIGN;
+  // outputs (dq, the workspace, every accumulator) against the inputs and
+  // each other
+  Range ins[4 + 2 * ATTN_RING_MAX_CHUNKS], outs[2 + 2 * ATTN_RING_MAX_CHUNKS];
+  int ni = 0, no = 0;
+  ins[ni++] = range(dout, qe * 2);
+  ins[ni++] = range(q, qe * 2);
+  ins[ni++] = range(out, qe * 2);
+  ins[ni++] = range(lse, lb);
+  outs[no++] = range(dq, qe * 2);
+  outs[no++] = range(workspace, (long long)need);
+  for (int c = 0; c < n_chunks; ++c) {
+    const long long ke = (long long)n * l_k_chunks[c] * h_kv * d;
+    ins[ni++] = range(k_chunks[c], ke * 2);
+    ins[ni++] = range(v_chunks[c], ke * 2);
+    outs[no++] = range(dk_acc_chunks[c], ke * 4);
+    outs[no++] = range(dv_acc_chunks[c], ke * 4);
+  }
+  for (int a = 0; a < no; ++a) {
+    for (int i = 0; i < ni; ++i)
+      if (overlap(outs[a], ins[i])) return ATTN_ERR_ALIAS;
+    for (int b2 = a + 1; b2 < no; ++b2)
+      if (overlap(outs[a], outs[b2])) return ATTN_ERR_ALIAS;
+  }
+  if (qe == 0) return ATTN_OK;  // no query rows: nothing to write or add
+  (void)hipGetLastError();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // no keys in any chunk: dQ = 0 (as 32-bit words), nothing added
+  if (!any_keys)
+    return finish(bea::launch_acc_init(static_cast<float*>(dq), nullptr, n, l_q, h, d / 2, hs));
+  bea::BwdChunkArgs ch[bea::kMaxChunks];
+  int m = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    if ((long long)n * l_k_chunks[c] == 0) continue;
+    int dlo, dhi;
+    mask_bounds(causal, win_l, win_r, q_offset, k_offsets[c], &dlo, &dhi);
+    ch[m++] = bea::BwdChunkArgs{k_chunks[c], v_chunks[c], dk_acc_chunks[c], dv_acc_chunks[c],
+                                l_k_chunks[c], dlo, dhi};
+  }
+  AttnShape s{n, l_q, ch[0].l_k, h, h_kv, d, scale, ch[0].dlo, ch[0].dhi, causal ? 1 : 0};
+  return finish(bea::launch_bwd_ring(dout, q, out, lse, ch, m, dq, s, workspace, hs));
+}
+
 int attn_bwd_static(const void* dout, const void* q, const void* k, const void* v,
                     const void* out, const float* lse, void* dq, void* dk, void* dv, int n,
                     int l_q, int l_k, int h, int h_kv, int d, float scale, int causal,

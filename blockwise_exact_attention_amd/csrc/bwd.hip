@@ -43,6 +43,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// One key/value chunk of the multi-chunk (ring share) kernels: its tensors,
+// its fp32 dK/dV accumulators, its mask bounds, its 128-key tiles and the
+// first dK/dV workgroup id that serves it.
+struct BwdChunk {
+  const uint16_t* k;
+  const uint16_t* v;
+  float* dk_acc;
+  float* dv_acc;
+  int l_k, dlo, dhi;
+  int ktiles;
+  int wg_begin;
+};
+
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -65,6 +78,9 @@ struct BwdParams {
   float c;      // scale * log2(e) (signed)
   float scale;
   int dlo, dhi;
+  // MULTI kernels: the chunks (the single-chunk fields above are unused)
+  BwdChunk ch[kMaxChunks];
+  int n_chunks;
 };
 
 // ------------------------------------------------------------ preprocess
@@ -126,9 +142,33 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
 constexpr int kKeysPerWave = 32;
 constexpr int kKeysPerWG = 4 * kKeysPerWave;
 
-template <int D, bool ACC>
+template <int D, bool ACC, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int n_ktiles,
                                                                int reverse) {
+  static_assert(!MULTI || ACC, "the multi-chunk form accumulates");
+  // MULTI: workgroups are numbered chunk by chunk; this one's chunk supplies
+  // the key side (tensors, accumulators, length, mask bounds, tiles)
+  // (kept in locals: p itself is never written, so that the chunk table is
+  // read from the kernel arguments instead of a private copy)
+  int wg = blockIdx.x;
+  const uint16_t* kp_ = p.k;
+  const uint16_t* vp_ = p.v;
+  float* dka_ = p.dk_acc;
+  float* dva_ = p.dv_acc;
+  int lk_ = p.l_k, dlo_ = p.dlo, dhi_ = p.dhi;
+  if constexpr (MULTI) {
+    int c = 0;
+    while (c + 1 < p.n_chunks && wg >= p.ch[c + 1].wg_begin) ++c;
+    wg -= p.ch[c].wg_begin;
+    n_ktiles = p.ch[c].ktiles;
+    kp_ = p.ch[c].k;
+    vp_ = p.ch[c].v;
+    dka_ = p.ch[c].dk_acc;
+    dva_ = p.ch[c].dv_acc;
+    lk_ = p.ch[c].l_k;
+    dlo_ = p.ch[c].dlo;
+    dhi_ = p.ch[c].dhi;
+  }
   constexpr int BQ = 64;         // query rows per tile
   constexpr int RB = D * 2;      // bytes per tile row
   constexpr int TB = BQ * RB;    // bytes per tile
@@ -157,8 +197,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
   // first key tiles are read by the most query rows: they go first
   const int heads = p.n * p.h_kv;
   const int tiles_heads = n_ktiles * heads;
-  const int slice = blockIdx.x / tiles_heads;
-  const int wid = blockIdx.x - slice * tiles_heads;
+  const int slice = wg / tiles_heads;
+  const int wid = wg - slice * tiles_heads;
   const int rank = wid / heads;
   const int kvh = wid - rank * heads;
   const int kt = reverse ? rank : n_ktiles - 1 - rank;
@@ -166,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
   const int g = kvh - b * p.h_kv;
   const int k0 = kt * kKeysPerWG;
   const int kw = k0 + wave * kKeysPerWave;
-  const int last_key = p.l_k - 1;
+  const int last_key = lk_ - 1;
   const int kj = kw + col;  // this lane's key (as B-operand column)
 
   const size_t kv_row = (size_t)p.h_kv * D;
@@ -175,12 +215,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
   // resident K and V rows of the wave's 32 keys
   u32x4_t kf[NDS], vf[NDS];
   {
-    const size_t off = ((size_t)b * p.l_k + min(kj, last_key)) * kv_row +
+    const size_t off = ((size_t)b * lk_ + min(kj, last_key)) * kv_row +
                        (size_t)g * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
-      kf[s] = *reinterpret_cast<const u32x4_t*>(p.k + off + 16 * s);
-      vf[s] = *reinterpret_cast<const u32x4_t*>(p.v + off + 16 * s);
+      kf[s] = *reinterpret_cast<const u32x4_t*>(kp_ + off + 16 * s);
+      vf[s] = *reinterpret_cast<const u32x4_t*>(vp_ + off + 16 * s);
     }
   }
   f32x16_t dkt[NDB], dvt[NDB];  // dK^T, dV^T: lane = key, regs = dims
@@ -194,8 +234,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
 
   // query rows that may see any key of this workgroup / wave
   const int kb_last = min(k0 + kKeysPerWG - 1, last_key);
-  const long long qlo = max(0LL, (long long)k0 - p.dhi);
-  const long long qhi = min((long long)p.l_q - 1, (long long)kb_last - p.dlo);
+  const long long qlo = max(0LL, (long long)k0 - dhi_);
+  const long long qhi = min((long long)p.l_q - 1, (long long)kb_last - dlo_);
   const bool wave_live = kw <= last_key;
   const int kw_last = min(kw + kKeysPerWave - 1, last_key);
 
@@ -258,9 +298,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
                   unsigned char* qn, unsigned char* on, float* ln) {
     if (u + 1 < u_end) load(u + 1, qn, on, ln);
     const int i0 = (t_begin + u % nt) * BQ;
-    const bool full = wave_live && (i0 + BQ <= p.l_q) && (kw + kKeysPerWave <= p.l_k) &&
-                      ((long long)kw - (i0 + BQ - 1) >= p.dlo) &&
-                      ((long long)(kw + kKeysPerWave - 1) - i0 <= p.dhi);
+    const bool full = wave_live && (i0 + BQ <= p.l_q) && (kw + kKeysPerWave <= lk_) &&
+                      ((long long)kw - (i0 + BQ - 1) >= dlo_) &&
+                      ((long long)(kw + kKeysPerWave - 1) - i0 <= dhi_);
     uint32_t ka = ka0;
     asm volatile("" : "+v"(ka));
     // S = Q K^T and dP = dO V^T: [32 queries x 32 keys] blocks, lane = key
@@ -281,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
         for (int r = 0; r < 16; ++r) {
           const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3);
           const int rel = kj - i;
-          const bool ok = (rel >= p.dlo) & (rel <= p.dhi) & (i < p.l_q) & (kj < p.l_k);
+          const bool ok = (rel >= dlo_) & (rel <= dhi_) & (i < p.l_q) & (kj < lk_);
           sa[qb][r] = ok ? sa[qb][r] : s_mask;
         }
     }
@@ -392,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
     // ---- split: every slice stores its partial dK^T, dV^T (fp32, the
     // lane's key and dims 32 db + 8 r4 + 4 half + 0..3); bwd_dkdv_reduce
     // adds them up (slice 0 first) and writes dK, dV
-    const size_t poff = ((size_t)b * p.l_k + kj) * kv_row + (size_t)g * D + 4 * half;
+    const size_t poff = ((size_t)b * lk_ + kj) * kv_row + (size_t)g * D + 4 * half;
     float* pk = p.part + (size_t)slice * 2 * p.part_half;
     if (kj <= last_key) {
 #pragma unroll
@@ -414,13 +454,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
     // ---- epilogue (ACC): dk_acc += scale dK^T, dv_acc += dV^T in fp32; the
     // lane owns key kj and dims 32 db + 8 r4 + 4 half + 0..3 (16 bytes)
     if (kj <= last_key) {
-      const size_t off = ((size_t)b * p.l_k + kj) * kv_row + (size_t)g * D + 4 * half;
+      const size_t off = ((size_t)b * lk_ + kj) * kv_row + (size_t)g * D + 4 * half;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4_t* k4 = reinterpret_cast<f32x4_t*>(p.dk_acc + off + 32 * db + 8 * r4);
-          f32x4_t* v4 = reinterpret_cast<f32x4_t*>(p.dv_acc + off + 32 * db + 8 * r4);
+          f32x4_t* k4 = reinterpret_cast<f32x4_t*>(dka_ + off + 32 * db + 8 * r4);
+          f32x4_t* v4 = reinterpret_cast<f32x4_t*>(dva_ + off + 32 * db + 8 * r4);
           const f32x4_t kx = {dkt[db][4 * r4], dkt[db][4 * r4 + 1], dkt[db][4 * r4 + 2],
                               dkt[db][4 * r4 + 3]};
           const f32x4_t vx = {dvt[db][4 * r4], dvt[db][4 * r4 + 1], dvt[db][4 * r4 + 2],
@@ -463,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
     const u32x4_t vk = *reinterpret_cast<const u32x4_t*>(stk + r * RB + c * 16);
     const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(stv + r * RB + c * 16);
     if (kw + r <= last_key) {
-      const size_t off = ((size_t)b * p.l_k + kw + r) * kv_row + (size_t)g * D + 8 * (ln % CPR);
+      const size_t off = ((size_t)b * lk_ + kw + r) * kv_row + (size_t)g * D + 8 * (ln % CPR);
       *reinterpret_cast<u32x4_t*>(p.dk + off) = vk;
       *reinterpret_cast<u32x4_t*>(p.dv + off) = vv;
     }
@@ -518,9 +558,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce(BwdParams p) {
 // over keys, so group 1's partial dQ^T is simply added to group 0's (through
 // LDS) before the epilogue.
 
-template <int D, bool ACC, int KSPLIT>
+template <int D, bool ACC, int KSPLIT, bool MULTI>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq_kernel(
     BwdParams p, int n_qtiles, int reverse) {
+  static_assert(!MULTI || !ACC, "the multi-chunk form writes dQ");
   constexpr int BN = 64;
   constexpr int RB = D * 2;
   constexpr int TB = BN * RB;
@@ -578,24 +619,34 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
 
-  const long long jlo = max(0LL, (long long)i0 + p.dlo);
-  const long long jhi = min((long long)p.l_k - 1,
-                            (long long)min(i0 + BM - 1, last_row) + p.dhi);
+  // MULTI: the key tiles of every chunk in turn, each with its own tensors,
+  // length and mask bounds, one dQ^T accumulation over all of them
+  const int n_ch = MULTI ? p.n_chunks : 1;
+  for (int ci = 0; ci < n_ch; ++ci) {
+  // the chunk's key side (locals: p is never written, see bwd_dkdv_kernel)
+  const uint16_t* kp_ = MULTI ? p.ch[ci].k : p.k;
+  const uint16_t* vp_ = MULTI ? p.ch[ci].v : p.v;
+  const int lk_ = MULTI ? p.ch[ci].l_k : p.l_k;
+  const int dlo_ = MULTI ? p.ch[ci].dlo : p.dlo;
+  const int dhi_ = MULTI ? p.ch[ci].dhi : p.dhi;
+  const long long jlo = max(0LL, (long long)i0 + dlo_);
+  const long long jhi = min((long long)lk_ - 1,
+                            (long long)min(i0 + BM - 1, last_row) + dhi_);
   const int wa = iw;
   const int wb = min(iw + 31, last_row);
   const bool wave_live = wa <= last_row;
-  const long long wjlo = max(0LL, (long long)wa + p.dlo);
-  const long long wjhi = min((long long)p.l_k - 1, (long long)wb + p.dhi);
-  const uint16_t* kbase = p.k + (size_t)b * p.l_k * kv_row + (size_t)g * D;
-  const uint16_t* vbase = p.v + (size_t)b * p.l_k * kv_row + (size_t)g * D;
+  const long long wjlo = max(0LL, (long long)wa + dlo_);
+  const long long wjhi = min((long long)lk_ - 1, (long long)wb + dhi_);
+  const uint16_t* kbase = kp_ + (size_t)b * lk_ * kv_row + (size_t)g * D;
+  const uint16_t* vbase = vp_ + (size_t)b * lk_ * kv_row + (size_t)g * D;
 
   const uint32_t lane_off = tile_lane_offset<D>(wave, lane, kv_row_b);
   uint32_t ka0, va0;
   lds_read_bases<D>(lane, ka0, va0);
   auto load = [&](int kt, unsigned char* kd, unsigned char* vd) {
     const long long j0 = (long long)kt * BN;
-    tile_dma<D>(kbase, j0, (long long)p.l_k - j0, kv_row_b, kd, wave, lane_off);
-    tile_dma<D>(vbase, j0, (long long)p.l_k - j0, kv_row_b, vd, wave, lane_off);
+    tile_dma<D>(kbase, j0, (long long)lk_ - j0, kv_row_b, kd, wave, lane_off);
+    tile_dma<D>(vbase, j0, (long long)lk_ - j0, kv_row_b, vd, wave, lane_off);
   };
 
   int kt_begin = 0, kt_end = 0;
@@ -610,8 +661,8 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
     const int j0 = kt * BN;
     const bool live = wave_live && (long long)j0 <= wjhi && (long long)(j0 + BN - 1) >= wjlo;
     if (live) {
-      const bool full = (j0 + BN <= p.l_k) && ((long long)j0 - wb >= p.dlo) &&
-                        ((long long)(j0 + BN - 1) - wa <= p.dhi);
+      const bool full = (j0 + BN <= lk_) && ((long long)j0 - wb >= dlo_) &&
+                        ((long long)(j0 + BN - 1) - wa <= dhi_);
       uint32_t ka = ka0, va = va0;
       asm volatile("" : "+v"(ka), "+v"(va));
       // S^T = K Q^T and dP^T = V dO^T: lane = query
@@ -635,7 +686,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
           for (int r = 0; r < 16; ++r) {
             const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
             const int rel = j - qi;
-            const bool ok = (rel >= p.dlo) & (rel <= p.dhi) & (j < p.l_k);
+            const bool ok = (rel >= dlo_) & (rel <= dhi_) & (j < lk_);
             sa[kb][r] = ok ? sa[kb][r] : s_mask;
           }
       }
@@ -696,6 +747,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
       }
     }
   }
+  }  // chunks
   if constexpr (KSPLIT == 2) {
     // ---- add group 1's partial dQ^T to group 0's through LDS (float4 f =
     // 4 db + r4 of lane wl at (f, wl), spread over the two V buffers)
@@ -817,7 +869,7 @@ template <int D, bool ACC>
 hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream, bool prepared) {
   if (!prepared) launch_pre_d<D>(p, stream);
   const int n_ktiles = (p.l_k + kKeysPerWG - 1) / kKeysPerWG;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, ACC>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, ACC, false>),
                      dim3((unsigned)(p.split * n_ktiles * p.n * p.h_kv)), dim3(kThreads),
                      0, stream, p, n_ktiles, causal ? 1 : 0);
   if (p.split > 1) {
@@ -831,15 +883,79 @@ hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream, bool
   const int n_qtiles = (p.l_q + 127) / 128;
   const long long dq_wgs = (long long)n_qtiles * p.n * p.h;
   if (dq_wgs < 2 * kDqCUs)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 2>), dim3((unsigned)dq_wgs), dim3(2 * kThreads),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 2, false>), dim3((unsigned)dq_wgs), dim3(2 * kThreads),
                        0, stream, p, n_qtiles, causal ? 1 : 0);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 1>), dim3((unsigned)dq_wgs), dim3(kThreads),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 1, false>), dim3((unsigned)dq_wgs), dim3(kThreads),
                        0, stream, p, n_qtiles, causal ? 1 : 0);
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_bwd_ring_d(const BwdParams& p, int total_wgs, int causal,
+                             hipStream_t stream) {
+  launch_pre_d<D>(p, stream);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), dim3((unsigned)total_wgs),
+                     dim3(kThreads), 0, stream, p, 0, causal ? 1 : 0);
+  const int n_qtiles = (p.l_q + 127) / 128;
+  const long long dq_wgs = (long long)n_qtiles * p.n * p.h;
+  if (dq_wgs < 2 * kDqCUs)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, 2, true>), dim3((unsigned)dq_wgs),
+                       dim3(2 * kThreads), 0, stream, p, n_qtiles, causal ? 1 : 0);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, 1, true>), dim3((unsigned)dq_wgs),
+                       dim3(kThreads), 0, stream, p, n_qtiles, causal ? 1 : 0);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_bwd_ring(const void* dout, const void* q, const void* out, const float* lse,
+                           const BwdChunkArgs* chunks, int n_chunks, void* dq,
+                           const AttnShape& s, void* workspace, hipStream_t stream) {
+  BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.o = static_cast<const uint16_t*>(out);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  const BwdWorkspace w = bwd_layout(s.n, s.l_q, 1, s.h, 1, s.d);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  p.dd = reinterpret_cast<float*>(ws + w.dd);
+  p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
+  p.split = 1;
+  p.n = s.n;
+  p.l_q = s.l_q;
+  p.h = s.h;
+  p.h_kv = s.h_kv;
+  p.grp = s.h / s.h_kv;
+  p.c = s.scale == 0.f ? 1e-30f : s.scale * kLog2e;
+  p.scale = s.scale;
+  p.n_chunks = n_chunks;
+  int wgs = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    BwdChunk& ch = p.ch[c];
+    ch.k = static_cast<const uint16_t*>(chunks[c].k);
+    ch.v = static_cast<const uint16_t*>(chunks[c].v);
+    ch.dk_acc = chunks[c].dk_acc;
+    ch.dv_acc = chunks[c].dv_acc;
+    ch.l_k = chunks[c].l_k;
+    ch.dlo = chunks[c].dlo;
+    ch.dhi = chunks[c].dhi;
+    ch.ktiles = (chunks[c].l_k + kKeysPerWG - 1) / kKeysPerWG;
+    ch.wg_begin = wgs;
+    wgs += ch.ktiles * s.n * s.h_kv;
+  }
+  // the single-chunk fields hold the first chunk (read only where the
+  // multi-chunk kernels have replaced them)
+  p.k = p.ch[0].k;
+  p.v = p.ch[0].v;
+  p.l_k = p.ch[0].l_k;
+  p.dlo = p.ch[0].dlo;
+  p.dhi = p.ch[0].dhi;
+  return s.d == 128 ? launch_bwd_ring_d<128>(p, wgs, s.causal, stream)
+                    : launch_bwd_ring_d<64>(p, wgs, s.causal, stream);
+}
 
 size_t bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d) {
   return bwd_layout(n, l_q, l_k, h, h_kv, d).total;

@@ -73,6 +73,23 @@ size_t bwd_prepared_bytes(int n, int l_q, int h);
 // workspace.
 hipError_t launch_bwd_prepare(const void* dout, const void* out, const float* lse, int n,
                               int l_q, int h, int d, void* workspace, hipStream_t stream);
+// One key/value chunk of the ring backward share: its tensors, its fp32 dK
+// and dV accumulators (gradients are added), length and mask bounds.
+struct BwdChunkArgs {
+  const void* k;
+  const void* v;
+  float* dk_acc;
+  float* dv_acc;
+  int l_k;
+  int dlo, dhi;
+};
+// The whole ring backward share in three launches: D and the base-2 LSE into
+// the workspace (bwd_prepared_bytes), every chunk's dK/dV added to its
+// accumulators, dQ over all chunks written (bf16) to dq.  Chunks non-empty,
+// 1..kMaxChunks of them.
+hipError_t launch_bwd_ring(const void* dout, const void* q, const void* out, const float* lse,
+                           const BwdChunkArgs* chunks, int n_chunks, void* dq,
+                           const AttnShape& s, void* workspace, hipStream_t stream);
 // dq_acc != nullptr: add the gradients to the fp32 accumulators (dq_acc,
 // dk_acc, dv_acc) instead of writing dq, dk, dv.  prepared: the workspace
 // already holds the rows launch_bwd_prepare writes (not recomputed).

@@ -312,6 +312,37 @@ int attn_bwd_acc_prepared(const void* dout, const void* q, const void* k, const 
                           void* stream, int dtype);
 
 /*
+ * attn_bwd_ring - one device's whole ring backward share in three launches
+ * (picotron RingAttentionFunc.backward / ring_attention_backward: the
+ * gradient of the share's queries against every chunk, D formed once from
+ * the saved global output; flash_sharding.py ring_bwd: dq summed over the
+ * chunks and cast to the query dtype).  For the share's query rows q with
+ * the forward share's final (out, lse) and the incoming dout:
+ *   dq            [n,l_q,h,d]    out  bfloat16: scale * sum over all chunks of
+ *                                     dS K (written, not accumulated)
+ *   dk_acc_chunks[c], dv_acc_chunks[c]
+ *                 [n,l_k_chunks[c],h_kv,d]  in/out  float32: chunk c's dK and
+ *                                     dV from these queries are ADDED (in a
+ *                                     ring these accumulators travel with the
+ *                                     chunk)
+ *   k_chunks, v_chunks, l_k_chunks, k_offsets as for attn_fwd_ring; the
+ *   pointer arrays (host, read during the call) hold n_chunks entries,
+ *   1 <= n_chunks <= ATTN_RING_MAX_CHUNKS.
+ *   workspace: at least attn_bwd_prepare_bytes(n, l_q, h) bytes of device
+ *   scratch (contents on entry do not matter).
+ * Equal, up to rounding order, to attn_bwd_acc per chunk with dQ accumulated
+ * in float32 and cast at the end.  bf16 only; d in {64, 128}.  No output may
+ * overlap an input or another output.
+ */
+int attn_bwd_ring(const void* dout, const void* q, const void* out, const float* lse,
+                  const void* const* k_chunks, const void* const* v_chunks,
+                  const int* l_k_chunks, const long long* k_offsets,
+                  float* const* dk_acc_chunks, float* const* dv_acc_chunks, int n_chunks,
+                  void* dq, int n, int l_q, int h, int h_kv, int d, float scale, int causal,
+                  int win_l, int win_r, long long q_offset, void* workspace,
+                  size_t workspace_bytes, void* stream, int dtype);
+
+/*
  * attn_bwd_static - attn_bwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same computation and results, with the workspace taken

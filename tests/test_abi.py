@@ -504,3 +504,42 @@ def test_bwd_prepare_checks():
     assert step(ws=None) == ATTN_ERR_WORKSPACE
     assert step(wsb=wneed - 1) == ATTN_ERR_WORKSPACE
     assert step(ws=ptrs[7]) == ATTN_ERR_ALIAS
+
+
+def test_bwd_ring_checks():
+    """The one-launch ring backward checks the chunk count, the host arrays,
+    every tensor and the workspace before any HIP call (fake addresses)."""
+    L = _lib.lib()
+    G = 7 << 32
+    H = 8 << 32
+
+    def call(n_chunks=2, arrays=True, l_k=(128, 64), k=(B, B + (1 << 30)),
+             dka=(F, F + (1 << 30)), dva=(G, G + (1 << 30)), dq=D_ + (1 << 28), ws=H,
+             wsb=None, dtype=ATTN_BF16, h=2, d=64):
+        m = max(n_chunks, 1)
+        pad = lambda t, x: list(t[:m]) + [x] * (m - len(t[:m]))
+        kp = (ctypes.c_void_p * m)(*pad(k, B))
+        vp = (ctypes.c_void_p * m)(*[C + (i << 30) for i in range(m)])
+        lk = (ctypes.c_int * m)(*pad(l_k, 16))
+        ko = (ctypes.c_longlong * m)(*[64 * i for i in range(m)])
+        ka = (ctypes.c_void_p * m)(*pad(dka, F))
+        va = (ctypes.c_void_p * m)(*pad(dva, G))
+        need = L.attn_bwd_prepare_bytes(1, 128, h) if wsb is None else wsb
+        return L.attn_bwd_ring(A, A + (1 << 28), D_, E, kp if arrays else None, vp, lk, ko,
+                               ka, va, n_chunks, dq, 1, 128, h, 2, d, 0.125, 1, -1, -1, 64,
+                               ws, need, None, dtype)
+    assert call(n_chunks=0) == ATTN_ERR_SHAPE
+    assert call(n_chunks=_lib.ATTN_RING_MAX_CHUNKS + 1) == ATTN_ERR_SHAPE
+    assert call(arrays=False) == ATTN_ERR_NULL
+    assert call(dq=None) == ATTN_ERR_NULL
+    assert call(dka=(F, None)) == ATTN_ERR_NULL
+    assert call(l_k=(128, -1)) == ATTN_ERR_SHAPE
+    assert call(h=3) == ATTN_ERR_SHAPE
+    assert call(d=96) == ATTN_ERR_UNSUPPORTED
+    assert call(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    assert call(ws=None) == ATTN_ERR_WORKSPACE
+    assert call(wsb=16) == ATTN_ERR_WORKSPACE
+    assert call(dka=(F + 8, F + (1 << 30))) == ATTN_ERR_ALIGN
+    assert call(dq=A + 64) == ATTN_ERR_ALIAS                 # dq over dout
+    assert call(dka=(F, F)) == ATTN_ERR_ALIAS                # two accumulators
+    assert call(dva=(G, B + (1 << 30) + 64)) == ATTN_ERR_ALIAS   # accumulator over a K chunk

@@ -140,12 +140,15 @@ def test_fp32_backward_is_rejected():
         A.attention_backward(q, q, q, q, q, lse)
 
 
-@pytest.mark.parametrize("d,h_kv,window,fused", [
-    (128, 2, (-1, -1), True),
-    (64, 1, (-1, -1), False),
-    (128, 2, (100, 0), True),
+@pytest.mark.parametrize("d,h_kv,window,fused,one_launch", [
+    (128, 2, (-1, -1), True, False),
+    (64, 1, (-1, -1), False, False),
+    (128, 2, (100, 0), True, False),
+    (128, 2, (-1, -1), True, True),
+    (64, 1, (-1, -1), False, True),
+    (128, 4, (100, 0), True, True),
 ])
-def test_ring_share_backward(d, h_kv, window, fused):
+def test_ring_share_backward(d, h_kv, window, fused, one_launch):
     """The ring backward as each of P = 4 ranks sees it (chunks of 96, causal):
     forward ring share for the rank's queries, then one attn_bwd_acc per
     chunk with the share's final (O, LSE).  dQ must equal the rank's rows of
@@ -162,14 +165,14 @@ def test_ring_share_backward(d, h_kv, window, fused):
     vc = [dev(v[:, s * c:(s + 1) * c], "bf16") for s in range(P)]
     offs = [s * c for s in range(P)]
     for r in range(P):
-        say(f"[ring bwd] d={d} h_kv={h_kv} window={window} rank {r}")
+        say(f"[ring bwd] d={d} h_kv={h_kv} window={window} one_launch={one_launch} rank {r}")
         qr, dor = q[:, r * c:(r + 1) * c], do[:, r * c:(r + 1) * c]
         tq, tdo = dev(qr, "bf16"), dev(dor, "bf16")
         out, lse = A.ring_share(tq, kc, vc, offs, r * c, scale, True,
                                 fused=fused, window=window)
         share = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, scale, True,
                                r * c, window)
-        dq, dk_acc, dv_acc = share.run(kc, vc, offs)
+        dq, dk_acc, dv_acc = share.run(kc, vc, offs, one_launch=one_launch)
         torch.cuda.synchronize()
         rq, rk, rv = oracle.attention_bwd(qr, k, v, dor, scale, True, window[0],
                                           window[1], r * c, 0)
@@ -179,6 +182,68 @@ def test_ring_share_backward(d, h_kv, window, fused):
                        f"rank {r} chunk {s} dk")
             check_grad(host(dv_acc[s]), rv[:, s * c:(s + 1) * c],
                        f"rank {r} chunk {s} dv")
+
+
+@pytest.mark.parametrize("seed", range(400, 406))
+def test_ring_backward_one_launch_random(seed):
+    """attn_bwd_ring on random chunk boundaries, orders (an empty chunk among
+    them), masks and head layouts: dq against the oracle's backward of the
+    query block over all keys, and each chunk's accumulator (which starts
+    from a random value) against that value plus the chunk's slice of the
+    oracle's dK, dV."""
+    r = np.random.default_rng(seed)
+    d = int(r.choice([64, 128]))
+    h_kv = int(r.choice([1, 2, 4]))
+    h = h_kv * int(r.choice([1, 2]))
+    l_q = int(r.integers(1, 300))
+    l_k = int(r.integers(1, 700))
+    nc = int(r.integers(1, 7))
+    cuts = sorted(int(x) for x in r.integers(0, l_k + 1, nc - 1))
+    bounds = [0, *cuts, l_k]
+    order = [int(x) for x in r.permutation(nc)]
+    causal = bool(r.integers(0, 2))
+    wl = int(r.choice([-1, -1, 60]))
+    wr = int(r.choice([-1, 0, 30]))
+    qo = int(r.integers(0, 700))
+    scale = float(r.choice([1.0 / math.sqrt(d), -0.07]))
+    say(f"[ring bwd one launch] seed {seed}: d={d} h={h} h_kv={h_kv} l_q={l_q} l_k={l_k} "
+        f"bounds={bounds} order={order} causal={causal} window=({wl},{wr}) qo={qo}")
+    q, k, v, do = (round_to_bf16(x) for x in draw_normal(
+        seed, [(1, l_q, h, d), (1, l_k, h_kv, d), (1, l_k, h_kv, d), (1, l_q, h, d)]))
+    tq, tk, tv, tdo = (dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = A.attention_forward(tq, tk, tv, scale, causal, (wl, wr), qo, 0)
+    kc = [dev(k[:, bounds[c]:bounds[c + 1]], "bf16") for c in order]
+    vc = [dev(v[:, bounds[c]:bounds[c + 1]], "bf16") for c in order]
+    offs = [bounds[c] for c in order]
+    init = [r.standard_normal((1, bounds[c + 1] - bounds[c], h_kv, d)).astype(np.float32)
+            for c in order]
+    dka = [torch.from_numpy(x.copy()).cuda() for x in init]
+    init_v = [r.standard_normal(x.shape).astype(np.float32) for x in init]
+    dva = [torch.from_numpy(x.copy()).cuda() for x in init_v]
+    dq = torch.empty_like(tq)
+    A.attn_bwd_ring(tdo, tq, o, lse, kc, vc, offs, dka, dva, dq, scale, causal, wl, wr, qo)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, scale, causal, wl, wr, qo, 0)
+    check_grad(host(dq), rq, "dq")
+    for i, c in enumerate(order):
+        sl = slice(bounds[c], bounds[c + 1])
+        check_grad(host(dka[i]) - init[i], rk[:, sl], f"chunk {c} dk")
+        check_grad(host(dva[i]) - init_v[i], rv[:, sl], f"chunk {c} dv")
+
+
+def test_ring_backward_without_keys():
+    """Chunks without keys: dq = 0, their (empty) accumulators untouched."""
+    q, do = (round_to_bf16(x) for x in draw_normal(71, [(1, 90, 4, 64), (1, 90, 4, 64)]))
+    tq, tdo = dev(q, "bf16"), dev(do, "bf16")
+    out = torch.zeros_like(tq)
+    lse = torch.full((1, 4, 90), float("-inf"), device="cuda")
+    empty = torch.zeros((1, 0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    eacc = torch.zeros((1, 0, 2, 64), dtype=torch.float32, device="cuda")
+    dq = torch.full_like(tq, float("nan"))
+    A.attn_bwd_ring(tdo, tq, out, lse, [empty, empty], [empty, empty], [0, 5],
+                    [eacc, eacc.clone()], [eacc.clone(), eacc.clone()], dq, 0.1, True)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0)
 
 
 def test_prepared_ring_steps_equal_unprepared():
@@ -234,16 +299,17 @@ def test_c3_ring_share_backward():
                             w.softmax_scale, True, fused=True)
     share = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, w.softmax_scale,
                            True, x["q_offset"])
-    dq, dk_acc, dv_acc = share.run(kc, vc, x["k_offsets"])
-    torch.cuda.synchronize()
     rq, rk, rv = oracle.attention_bwd(x["q"], x["k_full"], x["v_full"], do,
                                       w.softmax_scale, True, -1, -1,
                                       x["q_offset"], 0, block=1024)
-    check_grad(host(dq), rq, "C3 rank 7 dq")
     c = w.l_k
-    for s in range(8):
-        check_grad(host(dk_acc[s]), rk[:, s * c:(s + 1) * c], f"C3 chunk {s} dk")
-        check_grad(host(dv_acc[s]), rv[:, s * c:(s + 1) * c], f"C3 chunk {s} dv")
+    for one in (False, True):
+        dq, dk_acc, dv_acc = share.run(kc, vc, x["k_offsets"], one_launch=one)
+        torch.cuda.synchronize()
+        check_grad(host(dq), rq, f"C3 rank 7 dq (one launch {one})")
+        for s in range(8):
+            check_grad(host(dk_acc[s]), rk[:, s * c:(s + 1) * c], f"C3 chunk {s} dk ({one})")
+            check_grad(host(dv_acc[s]), rv[:, s * c:(s + 1) * c], f"C3 chunk {s} dv ({one})")
 
 
 @pytest.mark.parametrize("causal,window,h_kv", [(True, (-1, -1), 2), (True, (40, 0), 1),
