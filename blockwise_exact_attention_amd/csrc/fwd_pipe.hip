@@ -648,9 +648,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     for (int w = max(n_g, 0); w < n_steps; ++w) __syncthreads();
 
     float ltot = pair_sum(lsum);
+    // the epilogue's per-lane addresses come from an opaque copy of the lane
+    // id: computed here, instead of being hoisted to the kernel start into
+    // registers the key loop has to spill (whose reloads then wait for every
+    // outstanding store)
+    uint32_t eln = (uint32_t)lane;
+    asm volatile("" : "+v"(eln));
+    const uint32_t ecol = eln & 31u, ehalf = eln >> 5;
+    const int eqi = iw + (int)ecol;
     // ACC: the accumulator's LSE of this lane's row, read (and waited for)
     // before the exchange barrier, after which group 0 may overwrite it
-    const size_t li = (size_t)head * p.l_q + min(qi, last_row);
+    const size_t li = (size_t)head * p.l_q + min(eqi, last_row);
     float la = 0.f;
     if constexpr (ACC) {
       la = p.lse_acc[li];
@@ -681,7 +689,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       // in the other
       auto xo = [&](int f, int w) -> float4& {
         float4* base = reinterpret_cast<float4*>(f < NF / 2 ? &v_lds0[0][0] : &v_lds1[0][0]);
-        return base[((f % (NF / 2)) * kWaves + w) * 64 + lane];
+        return base[((f % (NF / 2)) * kWaves + w) * 64 + eln];
       };
       float2* xml = xml_lds;
       const int partner = (wave_all + WPG) % kWaves;
@@ -690,9 +698,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
         const int i = f / 4, r = 4 * (f % 4);
         xo(f, wave_all) = make_float4(give[i][r], give[i][r + 1], give[i][r + 2], give[i][r + 3]);
       }
-      xml[wave_all * 64 + lane] = make_float2(m, ltot);
+      xml[wave_all * 64 + eln] = make_float2(m, ltot);
       __syncthreads();
-      const float2 ml = xml[partner * 64 + lane];
+      const float2 ml = xml[partner * 64 + eln];
       // group 0's and group 1's (m, l), combined in one fixed order so both
       // groups get the same merged values
       const float m0 = grp == 0 ? m : ml.x, l0 = grp == 0 ? ltot : ml.y;
@@ -759,13 +767,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       static_assert(16 * CH * 16 <= 32 * RB, "16 fp32 rows fit the slice");
 #pragma unroll
       for (int round = 0; round < 2; ++round) {
-        if ((col >> 4) == round) {
-          const uint32_t row = (uint32_t)col & 15u;
+        if ((ecol >> 4) == (uint32_t)round) {
+          const uint32_t row = ecol & 15u;
 #pragma unroll
           for (int i = 0; i < NDBH; ++i)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-              const uint32_t cc = (uint32_t)(8 * i + 2 * r4) + (uint32_t)half;
+              const uint32_t cc = (uint32_t)(8 * i + 2 * r4) + ehalf;
               const f32x4_t x = {fin[i][4 * r4] * wb, fin[i][4 * r4 + 1] * wb,
                                  fin[i][4 * r4 + 2] * wb, fin[i][4 * r4 + 3] * wb};
               *reinterpret_cast<f32x4_t*>(fst + row * (4 * CH) + 4 * (cc ^ (2u * row % CH))) = x;
@@ -774,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int it = 0; it < 16 * CH / 64; ++it) {
-          const int k = it * 64 + lane;
+          const int k = it * 64 + (int)eln;
           const int rr = k / CH, cc = k % CH;
           const int src = 16 * round + rr;  // the lane that holds this row
           const int rmode = __shfl(mode, src);
@@ -793,7 +801,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       }
       // both groups read the accumulator's LSE before the exchange barrier;
       // only group 0 writes the new one
-      if (grp == 0 && half == 0 && qi <= last_row && (mode == 1 || mode == 2))
+      if (grp == 0 && ehalf == 0 && eqi <= last_row && (mode == 1 || mode == 2))
         p.lse_acc[li] = lnew;
     } else {
       // normalise and stage the 32 rows (bf16, 16-byte chunks swizzled by row
@@ -806,25 +814,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
           u32x2_t w;
           w[0] = pack_bf16x2(fin[i][4 * r4] * inv, fin[i][4 * r4 + 1] * inv);
           w[1] = pack_bf16x2(fin[i][4 * r4 + 2] * inv, fin[i][4 * r4 + 3] * inv);
-          const uint32_t cc = (uint32_t)(4 * (db0 + i) + r4) ^ chunk_swz<D>((uint32_t)col);
-          *reinterpret_cast<u32x2_t*>(stage + col * RB + cc * 16 + 8 * half) = w;
+          const uint32_t cc = (uint32_t)(4 * (db0 + i) + r4) ^ chunk_swz<D>(ecol);
+          *reinterpret_cast<u32x2_t*>(stage + ecol * RB + cc * 16 + 8 * ehalf) = w;
         }
       // the wave reads back what its own lanes wrote: LDS operations of one
       // wave complete in order once counted down
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       constexpr int CPH = NDBH * 4;   // 16-byte chunks finished per row
       constexpr int RPI = 64 / CPH;   // rows per store instruction
+      constexpr int NST = 32 / RPI;   // store instructions
+      // every read first, then the stores (no wait between stores)
+      u32x4_t val[NST];
+      const uint32_t c = 4u * (uint32_t)db0 + eln % CPH;
 #pragma unroll
-      for (int x = 0; x < 32 / RPI; ++x) {
-        const int r = x * RPI + lane / CPH;
-        const uint32_t c = (uint32_t)(4 * db0 + lane % CPH);
-        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(
-            stage + r * RB + (c ^ chunk_swz<D>((uint32_t)r)) * 16);
-        if (iw + r <= last_row)
-          *reinterpret_cast<u32x4_t*>(p.o + ((size_t)b * p.l_q + iw + r) * q_row +
-                                      (size_t)hq * D + 8 * c) = val;
+      for (int x = 0; x < NST; ++x) {
+        const uint32_t r = (uint32_t)(x * RPI) + eln / CPH;
+        val[x] = *reinterpret_cast<const u32x4_t*>(stage + r * RB +
+                                                   (c ^ chunk_swz<D>(r)) * 16);
       }
-      if (grp == 0 && half == 0 && qi <= last_row) p.lse[(size_t)head * p.l_q + qi] = lse_b;
+      uint16_t* const obase = p.o + ((size_t)b * p.l_q + iw) * q_row + (size_t)hq * D;
+#pragma unroll
+      for (int x = 0; x < NST; ++x) {
+        const uint32_t r = (uint32_t)(x * RPI) + eln / CPH;
+        if (iw + (int)r <= last_row)
+          *reinterpret_cast<u32x4_t*>(obase + (size_t)r * q_row + 8 * c) = val[x];
+      }
+      if (grp == 0 && ehalf == 0 && eqi <= last_row) p.lse[(size_t)head * p.l_q + eqi] = lse_b;
     }
   };
 
@@ -855,9 +870,10 @@ constexpr int kCUs = 256;
 // The pipelined loop pays more per q tile (a deeper prologue, the two-phase
 // fill and drain) than the one-phase kernel of fwd.hip and gains per key
 // tile: it is the better kernel once q tiles see this many key tiles on
-// average (measured on gfx950: about 16 tiles per q tile favour the
-// one-phase kernel, 128 and more the pipelined one).
-constexpr int kPipeMinTiles = 64;
+// average (measured on gfx950: 16-17 per 128-row q tile, the causal
+// 2 x 2048-token and the 1024-key ring step workloads, already favour it by
+// 3-10%; the 256-key window's 6-7 favour the one-phase kernel by 40%).
+constexpr int kPipeMinTiles = 12;
 
 int tiles_of(const PipeParams& p, int rows, int tile) {
   const int i0 = tile * rows;

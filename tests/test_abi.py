@@ -437,19 +437,23 @@ def test_bwd_wrapper_consistent_host_tensors_reach_the_device_check(acc):
 
 
 def test_fwd_kernel_name_reports_the_dispatch():
-    """Host-side dispatch: short key loops run the one-phase kernel, long
-    ones (64 and more key tiles per q tile on average) the pipelined one;
-    rejected or kernel-free calls name nothing."""
+    """Host-side dispatch: short key loops (the 256-key window) run the
+    one-phase kernel, longer ones (12 and more key tiles per 128-row q tile
+    on average) the pipelined one; rejected or kernel-free calls name
+    nothing."""
     from blockwise_exact_attention_amd.attention import fwd_kernel_name
     import torch
-    assert fwd_kernel_name(2, 2048, 2048, 16, 16, 128, True).startswith("fwd_bf16_kernel<128")
+    assert fwd_kernel_name(2, 2048, 2048, 16, 16, 128, True).startswith("fwd_pipe_kernel<128")
     assert fwd_kernel_name(4, 4096, 4096, 16, 16, 64, True, 256, 0).startswith(
         "fwd_bf16_kernel<64")
+    assert fwd_kernel_name(1, 700, 700, 2, 2, 128, True).startswith("fwd_bf16_kernel<128")
     assert fwd_kernel_name(1, 16384, 16384, 16, 16, 128, True).startswith("fwd_pipe_kernel<128")
     assert fwd_kernel_name(1, 1024, 8192, 32, 8, 128, True, q_offset=7168).startswith(
         "fwd_pipe_kernel<128")
     assert fwd_kernel_name(1, 1024, 1024, 32, 8, 128, True, q_offset=7168,
-                           fused=True).endswith("true>")
+                           fused=True) == "fwd_pipe_kernel<128, 2, true, false>"
+    assert fwd_kernel_name(1, 512, 512, 4, 4, 128, True,
+                           fused=True) == "fwd_bf16_kernel<128, 64, 2, true>"
     assert fwd_kernel_name(1, 128, 128, 2, 2, 64, dtype=torch.float32) == "fwd_f32_kernel<64>"
     assert fwd_kernel_name(1, 128, 128, 2, 2, 64, dtype=torch.float32, fused=True) is None
     assert fwd_kernel_name(1, 0, 128, 2, 2, 64) is None
