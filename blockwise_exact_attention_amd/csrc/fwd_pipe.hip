@@ -306,18 +306,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     const Cur cur0 = cur_at(grp);
     Cur curV = cur_next(cur0);
     Cur curK = cur_next(curV);
+    // only Q and the first K tile before the first scores: V of the first
+    // tile and K of the second are loaded between those products (the
+    // prologue's loads are bound by the CU's load rate, so this hides the
+    // first tile's compute behind them)
     if (n_g > 0) {
-      const auto rk = kv_rsrc(cur0, false), rv = kv_rsrc(cur0, true);
+      const auto rk = kv_rsrc(cur0, false);
 #pragma unroll
-      for (int x = 0; x < KV_DMA; ++x) {
-        dma_kv(rk, k_lds0[grp], x);
-        dma_kv(rv, v_lds0[grp], x);
-      }
-    }
-    if (n_g > 1) {
-      const auto rk = kv_rsrc(curV, false);
-#pragma unroll
-      for (int x = 0; x < KV_DMA; ++x) dma_kv(rk, k_lds1[grp], x);
+      for (int x = 0; x < KV_DMA; ++x) dma_kv(rk, k_lds0[grp], x);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
@@ -586,15 +582,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       }
     };
 
-    // ---- first tile: scores and softmax half, nothing to overlap yet
+    // ---- first tile: scores and softmax half, with the loads of V of the
+    // first tile and K of the second spread between the products
     if (n_g > 0) {
+      const auto rv = kv_rsrc(cur0, true);
+      const auto rk1 = kv_rsrc(curV, false);   // zero-length past the last tile
+      constexpr int NDMA0 = 2 * KV_DMA;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int s = 0; s < NDS; ++s) {
+          const int x = kb * NDS + s;
           const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&k_lds0[0][0] + kad[s] +
                                                              kb * 32 * RB);
           sA[kb] = mfma32x32x16(a, qf[s], s == 0 ? f32x16_t{} : sA[kb]);
+#pragma unroll
+          for (int d = 0; d < NDMA0; ++d) {
+            if (d * NSLOT / NDMA0 != x) continue;
+            if (d < KV_DMA) dma_kv(rv, v_lds0[grp], d);
+            else dma_kv(rk1, k_lds1[grp], d - KV_DMA);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       const TileInfo ti = tile_info(cur0);
       if (!ti.full) apply_mask(sA, tile_bits(ti));
@@ -602,7 +610,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
 #pragma unroll
       for (int k = 0; k < NSTAGE_A; ++k) soft_a(sA, k, z);
     }
-    // every wave is done with the first K buffer before it is refilled
+    // V of the first tile and K of the second have landed, and every wave
+    // is done with the first K buffer before it is refilled
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
 
     // ---- key loop: step u computes S of tile u+1 and O += P_u V_u; this
