@@ -869,7 +869,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
 // pairing of q tiles r and n_qtiles-1-r, or KSPLIT = 1 (256-row q tiles).
 // One workgroup per CU; the choice minimises max(longest workgroup, total /
 // CUs) in units of one step (eight waves x 32 rows x 64 keys), the
-// single-group step charged a little less (half the K/V loads per step).
+// single-group step charged a little less (half the K/V loads per step) and
+// pairing preferred on a tie (the long tile finds the short one's keys in
+// L2, and no second round of workgroups starts cold).
 struct PipeSchedule {
   int ksplit;
   int pairs;
@@ -915,7 +917,7 @@ PipeSchedule pick_pipe_schedule(const PipeParams& p, bool allow_ks1) {
         sum += len;
       }
       const double cost =
-          (ks == 1 ? 0.97 : 1.0) * std::max((double)mx, (double)sum * heads / kCUs);
+          (ks == 1 ? 0.97 : 1.0) * (pr ? 0.99 : 1.0) * std::max((double)mx, (double)sum * heads / kCUs);
       if (cost < best) {
         best = cost;
         out = PipeSchedule{ks, pr};
