@@ -1,6 +1,6 @@
 """Benchmark of the blockwise exact-attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--no-extras] [--no-cpu]
     python bench.py --workload {c3-steps,c3-fused,c3-share,c3-bwd,c3-bwd-one,c4,c5-fwd,c5-bwd}
 
 Workload: causal multi-head attention, n=2, l=2048, h=h_kv=16, d=128, bf16,
@@ -13,7 +13,10 @@ launch and backward; the sliding window; the 16k-token forward and backward;
 the merge's bandwidth warm and cold on both shapes against a plain streaming
 copy), and the fp64 CPU oracle's rate on a bounded sample of the headline
 workload.  --workload times one workload's call alone (for profiler runs);
---merge-only runs just the merge figures.
+--merge-only runs just the merge figures.  Every timed loop is preceded by
+--settle-ms (default 100) of the same calls back to back and then its warmup
+calls: the GPU reaches its sustained shader clock only after some 30 ms of
+continuous work.
 """
 from __future__ import annotations
 
@@ -32,6 +35,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
+SETTLE_MS = 100.0
 
 
 def parse():
@@ -39,6 +43,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="milliseconds of back-to-back calls before each timed "
+                         "loop's warmup, so that the loop runs at the clock the "
+                         "GPU holds under sustained work (0: none)")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline workload (and the CPU baseline)")
     ap.add_argument("--workload", default="c2",
@@ -60,10 +68,32 @@ def parse():
     return ap.parse_args()
 
 
+def settle(fn, torch, ms=None):
+    """Call fn() back to back for `ms` milliseconds of wall time (checked
+    every 8 calls).  The GPU raises its shader clock only after tens of
+    milliseconds of sustained work and lowers it again within milliseconds of
+    idling, so every timed loop starts with this, then its warmup calls.
+    Returns the number of calls made."""
+    ms = SETTLE_MS if ms is None else ms
+    calls = 0
+    if ms <= 0:
+        return calls
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn()
+        calls += 8
+        torch.cuda.synchronize()
+    return calls
+
+
 def timed(fn, steps, warmup, torch):
     """Mean GPU time per call (ms) of fn(), called `steps` times back to back
     between one event pair on the current stream (the one every library call
-    is launched on), so that the events' own cost is spread over the calls."""
+    is launched on), so that the events' own cost is spread over the calls.
+    The calls run at the settled clock (settle() first)."""
+    settle(fn, torch)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -317,7 +347,9 @@ def copy_calibration(nbytes):
 
 
 def main():
+    global SETTLE_MS
     args = parse()
+    SETTLE_MS = args.settle_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}): the "
               "path runs on one GPU's share; its multi-GPU form is not provided",
@@ -365,6 +397,7 @@ def main():
     def step():
         A.attn_fwd(tq, tk, tv, out, lse, w.softmax_scale, True)
 
+    settle_calls = settle(step, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -393,6 +426,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
+        "settle_calls": settle_calls,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
