@@ -428,8 +428,8 @@ class _Attention(torch.autograd.Function):
 def flash_attention(q, k, v, scale=None, causal=False, window=(-1, -1),
                     q_offset=0, k_offset=0, return_lse=False):
     """Differentiable exact attention: O (and LSE with return_lse) from
-    attn_fwd, gradients of q, k, v from attn_bwd (bf16 only for the
-    backward).  scale defaults to 1/sqrt(d)."""
+    attn_fwd, gradients of q, k, v from attn_bwd (bf16 or float32).  scale
+    defaults to 1/sqrt(d)."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     o, lse = _Attention.apply(q, k, v, float(scale), bool(causal),

@@ -150,9 +150,9 @@ int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
                  long long q_offset, long long k_offset, void* stream, int dtype) {
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  const long long qb = (long long)n * l_q * h * d * 2;
-  const long long kb = (long long)n * l_k * h_kv * d * 2;
+  const long long es = dtype == ATTN_F32 ? 4 : 2;
+  const long long qb = (long long)n * l_q * h * d * es;
+  const long long kb = (long long)n * l_k * h_kv * d * es;
   const long long ab = (long long)n * l_q * h * d * 4;
   const long long lb = (long long)n * h * l_q * 4;
   if (missing(q, qb) || missing(k, kb) || missing(v, kb) || missing(out_acc, ab) ||
@@ -179,6 +179,8 @@ int attn_fwd_acc(const void* q, const void* k, const void* v, float* out_acc,
   const bea::FwdChunk ch{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), l_k,
                          s.dlo, s.dhi};
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_F32)
+    return finish(bea::launch_fwd_f32(q, k, v, nullptr, nullptr, s, hs, out_acc, lse_acc));
   if (bea::fwd_pipe_preferred(&ch, 1, s))
     return finish(bea::launch_fwd_pipe(q, &ch, 1, nullptr, nullptr, s, hs, out_acc, lse_acc));
   return finish(bea::launch_fwd_bf16(q, k, v, nullptr, nullptr, s, hs, out_acc, lse_acc));
@@ -188,11 +190,15 @@ const char* attn_fwd_kernel_name(int n, int l_q, int l_k, int h, int h_kv, int d
                                  int causal, int win_l, int win_r, long long q_offset,
                                  long long k_offset, int dtype, int fused) {
   if (check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype) != ATTN_OK) return nullptr;
-  if (fused && dtype != ATTN_BF16) return nullptr;
   if ((long long)n * l_q == 0 || l_k == 0) return nullptr;  // no attention kernel runs
   AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
   mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
-  if (dtype == ATTN_F32) return d == 128 ? "fwd_f32_kernel<128>" : "fwd_f32_kernel<64>";
+  if (dtype == ATTN_F32) {
+    static const char* const names[2][2] = {
+        {"fwd_f32_kernel<64, false>", "fwd_f32_kernel<64, true>"},
+        {"fwd_f32_kernel<128, false>", "fwd_f32_kernel<128, true>"}};
+    return names[d == 128 ? 1 : 0][fused ? 1 : 0];
+  }
   const bea::FwdChunk ch{nullptr, nullptr, l_k, s.dlo, s.dhi};
   if (bea::fwd_pipe_preferred(&ch, 1, s)) return bea::fwd_pipe_kernel_name(&ch, 1, s, fused);
   return bea::fwd_bf16_kernel_name(s, fused);
@@ -380,8 +386,8 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
               bool prepared = false) {
   int st = check_attn_args(n, l_q, l_k, h, h_kv, d, scale, dtype);
   if (st != ATTN_OK) return st;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  const long long es = 2;              // bf16 inputs
+  const bool f32 = dtype == ATTN_F32;
+  const long long es = f32 ? 4 : 2;    // input element bytes
   const long long gb = acc ? 4 : es;   // gradient element bytes
   const long long qe = (long long)n * l_q * h * d;
   const long long ke = (long long)n * l_k * h_kv * d;
@@ -437,6 +443,10 @@ int bwd_entry(const void* dout, const void* q, const void* k, const void* v,
   }
   AttnShape s{n, l_q, l_k, h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
   mask_bounds(causal, win_l, win_r, q_offset, k_offset, &s.dlo, &s.dhi);
+  if (f32)
+    return finish(bea::launch_bwd_f32(dout, q, k, v, out, lse, static_cast<float*>(dq),
+                                      static_cast<float*>(dk), static_cast<float*>(dv), s,
+                                      workspace, acc, prepared, hs));
   if (acc)
     return finish(bea::launch_bwd(dout, q, k, v, out, lse, nullptr, nullptr, nullptr,
                                   s, workspace, true, hs, static_cast<float*>(dq),
@@ -483,7 +493,7 @@ int attn_bwd_prepare(const void* dout, const void* out, const float* lse, int n,
   // the query-side checks of the backward, with one key/value head
   int st = check_attn_args(n, l_q, 0, h, 1, d, 0.f, dtype);
   if (st != ATTN_OK) return st;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const long long es = dtype == ATTN_F32 ? 4 : 2;
   const long long qe = (long long)n * l_q * h * d;
   const long long lb = (long long)n * h * l_q * 4;
   if (missing(dout, qe) || missing(out, qe) || missing(lse, lb)) return ATTN_ERR_NULL;
@@ -493,12 +503,14 @@ int attn_bwd_prepare(const void* dout, const void* out, const float* lse, int n,
   if (!aligned(dout, 16) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
     return ATTN_ERR_ALIGN;
   const Range rw = range(workspace, (long long)need);
-  if (overlap(rw, range(dout, qe * 2)) || overlap(rw, range(out, qe * 2)) ||
+  if (overlap(rw, range(dout, qe * es)) || overlap(rw, range(out, qe * es)) ||
       overlap(rw, range(lse, lb)))
     return ATTN_ERR_ALIAS;
   (void)hipGetLastError();
-  return finish(bea::launch_bwd_prepare(dout, out, lse, n, l_q, h, d, workspace,
-                                        static_cast<hipStream_t>(stream)));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_F32)
+    return finish(bea::launch_bwd_f32_prepare(dout, out, lse, n, l_q, h, d, workspace, hs));
+  return finish(bea::launch_bwd_prepare(dout, out, lse, n, l_q, h, d, workspace, hs));
 }
 
 int attn_bwd_acc_prepared(const void* dout, const void* q, const void* k, const void* v,

@@ -966,6 +966,13 @@ size_t bwd_prepared_bytes(int n, int l_q, int h) {
   return bwd_layout(n, l_q, 1, h, 1, 64).part;
 }
 
+void bwd_prepared_rows(void* workspace, int n, int l_q, int h, float** dd, float** lse2) {
+  const BwdWorkspace w = bwd_layout(n, l_q, 1, h, 1, 64);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  *dd = reinterpret_cast<float*>(ws + w.dd);
+  *lse2 = reinterpret_cast<float*>(ws + w.lse2);
+}
+
 hipError_t launch_bwd_prepare(const void* dout, const void* out, const float* lse, int n,
                               int l_q, int h, int d, void* workspace, hipStream_t stream) {
   BwdParams p{};

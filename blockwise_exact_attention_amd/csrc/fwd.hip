@@ -564,12 +564,14 @@ struct FwdF32Params {
   float c;          // |scale| * log2(e)
   int neg_scale;    // 1: scale < 0 (Q enters negated)
   int dlo, dhi;
+  float* acc;       // ACC: the fp32 ring accumulator merged into
+  float* lse_acc;
 };
 
 constexpr int kF32Rows = 64;
 constexpr int kF32Keys = 64;
 
-template <int D>
+template <int D, bool ACC>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdF32Params p) {
   constexpr int NC = D / 16;  // float4 chunks per lane
   __shared__ f32x4_t ks[kF32Keys * (D / 4)];
@@ -666,14 +668,41 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdF32Params p) {
   }
   if (qi <= last_row) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    f32x4_t* optr = reinterpret_cast<f32x4_t*>(
-        p.o + ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D);
+    const float muse = (m == kNegInf) ? 0.f : m;
+    const float lse_blk = lsum > 0.f ? (muse + log2f(lsum)) * kLn2 : kNegInf;
+    const size_t orow = ((size_t)b * p.l_q + qi) * q_row + (size_t)hq * D;
+    const size_t li = (size_t)head * p.l_q + qi;
+    if (!ACC) {
+      f32x4_t* optr = reinterpret_cast<f32x4_t*>(p.o + orow);
 #pragma unroll
-    for (int m4 = 0; m4 < NC; ++m4) optr[c + 4 * m4] = ov[m4] * inv;
-    if (c == 0) {
-      const float muse = (m == kNegInf) ? 0.f : m;
-      p.lse[(size_t)head * p.l_q + qi] =
-          lsum > 0.f ? (muse + log2f(lsum)) * kLn2 : kNegInf;
+      for (int m4 = 0; m4 < NC; ++m4) optr[c + 4 * m4] = ov[m4] * inv;
+      if (c == 0) p.lse[li] = lse_blk;
+    } else {
+      // the merge of (O / l, lse_blk) into the accumulator row, with the
+      // merge kernel's weights and -inf guards: an empty block keeps the
+      // row (or clears it when the row is empty too), an empty accumulator
+      // row takes the block
+      f32x4_t* aptr = reinterpret_cast<f32x4_t*>(p.acc + orow);
+      const float a = p.lse_acc[li];  // read by all four lanes before lane 0 writes
+      if (lse_blk == kNegInf) {
+        if (a == kNegInf) {
+#pragma unroll
+          for (int m4 = 0; m4 < NC; ++m4) aptr[c + 4 * m4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      } else if (a == kNegInf) {
+#pragma unroll
+        for (int m4 = 0; m4 < NC; ++m4) aptr[c + 4 * m4] = ov[m4] * inv;
+        if (c == 0) p.lse_acc[li] = lse_blk;
+      } else {
+        const float mx = fmaxf(a, lse_blk);
+        const float mn = fminf(a, lse_blk);
+        const float lse = mx + log1pf(expf(mn - mx));
+        const float wa = expf(a - lse);
+        const float wb = expf(lse_blk - lse) * inv;
+#pragma unroll
+        for (int m4 = 0; m4 < NC; ++m4) aptr[c + 4 * m4] = aptr[c + 4 * m4] * wa + ov[m4] * wb;
+        if (c == 0) p.lse_acc[li] = lse;
+      }
     }
   }
 }
@@ -804,7 +833,7 @@ const char* fwd_bf16_kernel_name(const AttnShape& s, bool acc) {
 
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
                           void* out, float* lse, const AttnShape& s,
-                          hipStream_t stream) {
+                          hipStream_t stream, float* acc, float* lse_acc) {
   FwdF32Params p;
   p.q = static_cast<const float*>(q);
   p.k = static_cast<const float*>(k);
@@ -821,13 +850,21 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
   p.neg_scale = s.scale < 0.f ? 1 : 0;
   p.dlo = s.dlo;
   p.dhi = s.dhi;
+  p.acc = acc;
+  p.lse_acc = lse_acc;
   const unsigned tiles = (unsigned)((s.l_q + kF32Rows - 1) / kF32Rows);
   dim3 grid(tiles * (unsigned)p.n_heads);
   dim3 block(256);
-  if (s.d == 128)
-    hipLaunchKernelGGL((fwd_f32_kernel<128>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_f32_kernel<64>), grid, block, 0, stream, p);
+  if (acc) {
+    if (s.d == 128)
+      hipLaunchKernelGGL((fwd_f32_kernel<128, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_f32_kernel<64, true>), grid, block, 0, stream, p);
+  } else if (s.d == 128) {
+    hipLaunchKernelGGL((fwd_f32_kernel<128, false>), grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((fwd_f32_kernel<64, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -47,9 +47,11 @@ bool fwd_pipe_preferred(const FwdChunk* chunks, int n_chunks, const AttnShape& s
 const char* fwd_bf16_kernel_name(const AttnShape& s, bool acc);
 const char* fwd_pipe_kernel_name(const FwdChunk* chunks, int n_chunks, const AttnShape& s,
                                  bool acc);
+// float32 forward; acc != nullptr merges into the accumulator as above.
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
                           void* out, float* lse, const AttnShape& s,
-                          hipStream_t stream);
+                          hipStream_t stream, float* acc = nullptr,
+                          float* lse_acc = nullptr);
 
 hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
                         const float* lse_blk, int n, int l, int h, int d,
@@ -69,10 +71,20 @@ size_t bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d);
 // Leading bytes of every backward workspace that hold the per-row D and
 // LSE * log2(e).
 size_t bwd_prepared_bytes(int n, int l_q, int h);
+// Where those rows sit in a workspace: D at *dd, LSE * log2(e) at *lse2.
+void bwd_prepared_rows(void* workspace, int n, int l_q, int h, float** dd, float** lse2);
 // Writes those rows (D = rowsum(dout * out), LSE in log2 units) into the
-// workspace.
+// workspace; dout and out bf16, or float32 for the _f32 form.
 hipError_t launch_bwd_prepare(const void* dout, const void* out, const float* lse, int n,
                               int l_q, int h, int d, void* workspace, hipStream_t stream);
+hipError_t launch_bwd_f32_prepare(const void* dout, const void* out, const float* lse, int n,
+                                  int l_q, int h, int d, void* workspace, hipStream_t stream);
+// The float32 backward: dq, dk, dv written (acc: added to) in float32; the
+// workspace's prepared rows are formed first unless `prepared`.
+hipError_t launch_bwd_f32(const void* dout, const void* q, const void* k, const void* v,
+                          const void* out, const float* lse, float* dq, float* dk, float* dv,
+                          const AttnShape& s, void* workspace, bool acc, bool prepared,
+                          hipStream_t stream);
 // One key/value chunk of the ring backward share: its tensors, its fp32 dK
 // and dV accumulators (gradients are added), length and mask bounds.
 struct BwdChunkArgs {

@@ -77,7 +77,8 @@ enum attn_status {
                                would exceed 2^31 workgroups, or a chunk count
                                outside 1..ATTN_RING_MAX_CHUNKS                   */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite
-                               scale, or fp32 backward / ring step / ring share  */
+                               scale, or fp32 one-launch ring share (forward
+                               or backward)                                      */
   ATTN_ERR_HIP = 4,         /* the HIP runtime reported a launch failure         */
   ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than required (or NULL when
                                required)                                         */
@@ -141,8 +142,8 @@ int attn_merge(float* out_acc, float* lse_acc, const void* out_blk,
  * or set to O = 0 when the accumulator row is at -inf too; an accumulator
  * row at -inf is replaced, whatever it held).
  *
- *   q       [n,l_q,h,d]     in      bfloat16 (dtype must be ATTN_BF16)
- *   k,v     [n,l_k,h_kv,d]  in      bfloat16
+ *   q       [n,l_q,h,d]     in      dtype (ATTN_BF16 or ATTN_F32)
+ *   k,v     [n,l_k,h_kv,d]  in      dtype
  *   out_acc [n,l_q,h,d]     in/out  float32
  *   lse_acc [n,h,l_q]       in/out  float32, natural log
  *   d in {64, 128}; any finite scale; masking as for attn_fwd.
@@ -233,7 +234,8 @@ int attn_acc_cast(const float* out_acc, void* out, int n, int l, int h, int d,
  *   dV = P^T dout; with grouped heads dK and dV of a key/value head sum over
  *   the query heads that read it.  Accumulation is float32.
  *
- *   dtype must be ATTN_BF16 (ATTN_F32 returns ATTN_ERR_UNSUPPORTED).
+ *   dtype ATTN_BF16 (MFMA kernels) or ATTN_F32 (float32 FMA kernels, every
+ *   product and sum in float32).
  *   dout, q, out [n,l_q,h,d] dtype in;  k, v [n,l_k,h_kv,d] dtype in
  *   lse [n,h,l_q] float32 in (as written by attn_fwd)
  *   dq [n,l_q,h,d], dk, dv [n,l_k,h_kv,d] dtype out
@@ -261,9 +263,9 @@ int attn_bwd(const void* dout, const void* q, const void* k, const void* v,
  * the full gradients.  dk_acc / dv_acc of a chunk collect the contributions
  * of every query block that reads it (in a real ring they travel with the
  * chunk).
- *   dout, q, out [n,l_q,h,d] bf16; k, v [n,l_k,h_kv,d] bf16; lse [n,h,l_q]
+ *   dout, q, out [n,l_q,h,d] dtype; k, v [n,l_k,h_kv,d] dtype; lse [n,h,l_q]
  *   dq_acc [n,l_q,h,d] float32 in/out; dk_acc, dv_acc [n,l_k,h_kv,d]
- *   float32 in/out; workspace as for attn_bwd; dtype must be ATTN_BF16.
+ *   float32 in/out; workspace as for attn_bwd; dtype ATTN_BF16 or ATTN_F32.
  * The accumulators must not overlap the inputs, the workspace or each other;
  * calls that add to the same accumulator must be ordered on one stream.
  */
@@ -291,7 +293,8 @@ size_t attn_bwd_workspace_bytes(int n, int l_q, int l_k, int h, int h_kv, int d)
  * attn_bwd_prepare writes, for the query rows of (dout, out, lse), D and the
  * LSE in base-2 units into the first attn_bwd_prepare_bytes(n, l_q, h)
  * bytes of `workspace` (at least that many; 16-byte aligned).  Shapes as
- * for attn_bwd; dtype must be ATTN_BF16.
+ * for attn_bwd; dtype ATTN_BF16 or ATTN_F32 (the rows are the same float32
+ * values either way, so a share prepares with the dtype of its dout, out).
  *
  * attn_bwd_acc_prepared is attn_bwd_acc (same arguments and workspace
  * size) without that preprocessing: it reads D and the LSE from the

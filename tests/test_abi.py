@@ -92,13 +92,17 @@ def _fwd_acc(**kw):
 
 
 def test_fwd_acc_argument_checks():
-    """The fused ring step rejects what attn_fwd rejects, and fp32 inputs
-    (the accumulator here is 128*2*64*4 = 64 KiB from D_)."""
+    """The fused ring step rejects what attn_fwd rejects (the accumulator
+    here is 128*2*64*4 = 64 KiB from D_); float32 inputs are checked with
+    their own element size."""
     for f in ("q", "k", "v", "acc", "lse"):
         assert _fwd_acc(**{f: None}) == ATTN_ERR_NULL
     assert _fwd_acc(h=6, h_kv=4) == ATTN_ERR_SHAPE
     assert _fwd_acc(d=96) == ATTN_ERR_UNSUPPORTED
-    assert _fwd_acc(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    # q is 32 KiB in bf16 and 64 KiB in float32: an accumulator 48 KiB past
+    # q overlaps only the float32 one
+    assert _fwd_acc(dtype=ATTN_F32, acc=A + 49152) == ATTN_ERR_ALIAS
+    assert _fwd_acc(dtype=ATTN_F32, lse=E + 2) == ATTN_ERR_ALIGN
     assert _fwd_acc(acc=D_ + 8) == ATTN_ERR_ALIGN
     assert _fwd_acc(lse=E + 2) == ATTN_ERR_ALIGN
     assert _fwd_acc(acc=A + 64) == ATTN_ERR_ALIAS
@@ -268,7 +272,11 @@ def test_bwd_checks():
     assert call(ptrs=bad) == ATTN_ERR_NULL
     assert call(h=3) == ATTN_ERR_SHAPE
     assert call(d=32) == ATTN_ERR_UNSUPPORTED
-    assert call(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    # dout is 32 KiB in bf16 and 64 KiB in float32: a dq 40 KiB past it
+    # overlaps only the float32 one
+    f32_alias = list(ptrs)
+    f32_alias[6] = A + 40960
+    assert call(ptrs=f32_alias, dtype=ATTN_F32) == ATTN_ERR_ALIAS
     assert call(ws=None) == ATTN_ERR_WORKSPACE
     assert call(wsb=need - 1) == ATTN_ERR_WORKSPACE
     alias = list(ptrs)
@@ -292,7 +300,11 @@ def test_bwd_static_checks():
     assert call(ptrs=bad) == ATTN_ERR_NULL
     assert call(h=3) == ATTN_ERR_SHAPE
     assert call(d=32) == ATTN_ERR_UNSUPPORTED
-    assert call(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    # dout is 32 KiB in bf16 and 64 KiB in float32: a dq 40 KiB past it
+    # overlaps only the float32 one
+    f32_alias = list(ptrs)
+    f32_alias[6] = A + 40960
+    assert call(ptrs=f32_alias, dtype=ATTN_F32) == ATTN_ERR_ALIAS
     alias = list(ptrs)
     alias[6] = ptrs[1]          # dq on top of q
     assert call(ptrs=alias) == ATTN_ERR_ALIAS
@@ -345,7 +357,9 @@ def test_bwd_acc_checks():
         bad = list(ptrs)
         bad[i] = None
         assert call(ptrs=bad) == ATTN_ERR_NULL
-    assert call(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    f32_alias = list(ptrs)
+    f32_alias[6] = A + 40960    # inside a float32 dout only
+    assert call(ptrs=f32_alias, dtype=ATTN_F32) == ATTN_ERR_ALIAS
     assert call(wsb=need - 1) == ATTN_ERR_WORKSPACE
     mis = list(ptrs)
     mis[6] = D_ + 4
@@ -454,8 +468,10 @@ def test_fwd_kernel_name_reports_the_dispatch():
                            fused=True) == "fwd_pipe_kernel<128, 2, true, false>"
     assert fwd_kernel_name(1, 512, 512, 4, 4, 128, True,
                            fused=True) == "fwd_bf16_kernel<128, 64, 2, true>"
-    assert fwd_kernel_name(1, 128, 128, 2, 2, 64, dtype=torch.float32) == "fwd_f32_kernel<64>"
-    assert fwd_kernel_name(1, 128, 128, 2, 2, 64, dtype=torch.float32, fused=True) is None
+    assert fwd_kernel_name(1, 128, 128, 2, 2, 64,
+                           dtype=torch.float32) == "fwd_f32_kernel<64, false>"
+    assert fwd_kernel_name(1, 128, 128, 2, 2, 128, dtype=torch.float32,
+                           fused=True) == "fwd_f32_kernel<128, true>"
     assert fwd_kernel_name(1, 0, 128, 2, 2, 64) is None
     assert fwd_kernel_name(1, 128, 0, 2, 2, 64) is None
     assert fwd_kernel_name(1, 128, 128, 2, 2, 96) is None
@@ -485,7 +501,7 @@ def test_bwd_prepare_checks():
     assert prep(dout=None) == ATTN_ERR_NULL
     assert prep(lse=None) == ATTN_ERR_NULL
     assert prep(d=96) == ATTN_ERR_UNSUPPORTED
-    assert prep(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    assert prep(dtype=ATTN_F32, ws=A + 40960) == ATTN_ERR_ALIAS   # inside a float32 dout only
     assert prep(l_q=-1) == ATTN_ERR_SHAPE
     assert prep(ws=None) == ATTN_ERR_WORKSPACE
     assert prep(wsb=need - 1) == ATTN_ERR_WORKSPACE
@@ -504,7 +520,9 @@ def test_bwd_prepare_checks():
     bad[2] = None
     assert step(ptrs=bad) == ATTN_ERR_NULL
     assert step(h=3) == ATTN_ERR_SHAPE
-    assert step(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    f32_alias = list(ptrs)
+    f32_alias[6] = A + 40960    # inside a float32 dout only
+    assert step(ptrs=f32_alias, dtype=ATTN_F32) == ATTN_ERR_ALIAS
     assert step(ws=None) == ATTN_ERR_WORKSPACE
     assert step(wsb=wneed - 1) == ATTN_ERR_WORKSPACE
     assert step(ws=ptrs[7]) == ATTN_ERR_ALIAS

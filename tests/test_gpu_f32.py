@@ -1,0 +1,195 @@
+"""GPU parity of the float32 paths against the fp64 oracle, through the C ABI:
+the float32 backward (attn_bwd, attn_bwd_acc, the prepared ring steps,
+attn_bwd_static, the ring backward share) and the float32 fused ring step
+(attn_fwd_acc and the fused ring share).  The GPU backward consumes the GPU
+forward's float32 O and LSE.
+
+Tolerance: the pages fix 1e-5 for float32 inputs.  O and LSE: 1e-5
+absolute; gradients: max |g - g_ref| <= 1e-5 * max(1, max |g_ref|), the same
+bound scaled to the gradient's magnitude as for the bf16 gradients."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from blockwise_exact_attention_amd import attention as A
+from blockwise_exact_attention_amd.inputs import draw_normal
+from blockwise_exact_attention_amd.workloads import WORKLOADS, make_inputs
+from gpu_util import check_o_lse, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def check_grad(g, ref, name):
+    sel = ~np.isnan(ref)
+    assert np.all(np.isfinite(g[sel])), f"{name}: non-finite"
+    bound = TOL * max(1.0, float(np.max(np.abs(ref[sel]), initial=0.0)))
+    err = float(np.max(np.abs(g[sel] - ref[sel]), initial=0.0))
+    say(f"  {name}: max|err| = {err:.3e} (tol {bound:.3e})")
+    assert err <= bound, f"{name}: {err} > {bound}"
+
+
+def fwd_bwd(q, k, v, do, scale, causal, wl=-1, wr=-1, qo=0, ko=0):
+    tq, tk, tv, tdo = (dev(x, "f32") for x in (q, k, v, do))
+    o, lse = A.attention_forward(tq, tk, tv, scale, causal, (wl, wr), qo, ko)
+    dq, dk, dv = A.attention_backward(tdo, tq, tk, tv, o, lse, scale, causal, (wl, wr), qo, ko)
+    torch.cuda.synchronize()
+    return (tq, tk, tv, tdo, o, lse), (host(dq), host(dk), host(dv))
+
+
+CASES = [
+    # n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko
+    (1, 128, 128, 2, 2, 64, False, -1, -1, 0, 0),      # the tiny fp32 workload
+    (1, 200, 333, 4, 2, 128, False, -1, -1, 0, 0),
+    (2, 150, 150, 4, 4, 64, True, -1, -1, 0, 0),
+    (1, 257, 300, 8, 2, 128, True, -1, -1, 43, 0),
+    (1, 130, 400, 3, 1, 64, True, 40, 7, 100, 0),      # MQA + window
+    (1, 96, 160, 4, 4, 64, True, -1, -1, 0, 64),       # rows 0..63 empty
+    (1, 64, 64, 2, 2, 128, True, -1, -1, 0, 1000),     # every row empty
+    (1, 1, 300, 2, 1, 128, True, -1, -1, 299, 0),      # single query
+    (1, 300, 1, 2, 2, 64, False, -1, -1, 0, 0),        # single key
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_f32_backward(case):
+    n, l_q, l_k, h, h_kv, d, causal, wl, wr, qo, ko = case
+    say(f"[f32 bwd] {case}")
+    q, k, v, do = draw_normal(21 + l_q + l_k + h, [(n, l_q, h, d), (n, l_k, h_kv, d),
+                                                  (n, l_k, h_kv, d), (n, l_q, h, d)])
+    scale = 1.0 / math.sqrt(d)
+    _, (dq, dk, dv) = fwd_bwd(q, k, v, do, scale, causal, wl, wr, qo, ko)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, scale, causal, wl, wr, qo, ko)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0, 0.4])
+def test_f32_backward_scales(scale):
+    q, k, v, do = draw_normal(31, [(1, 200, 2, 64), (1, 180, 1, 64), (1, 180, 1, 64),
+                                   (1, 200, 2, 64)])
+    _, (dq, dk, dv) = fwd_bwd(q, k, v, do, scale, True, -1, -1, 20, 0)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, scale, True, -1, -1, 20, 0)
+    if scale == 0.0:
+        assert not np.any(dq) and not np.any(dk)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
+def test_f32_backward_accumulating_prepared_and_static():
+    """attn_bwd_acc adds this backward to float32 accumulators; the prepared
+    form equals it bit for bit, and attn_bwd_static equals attn_bwd."""
+    n, l_q, l_k, h, h_kv, d = 1, 190, 250, 4, 2, 128
+    q, k, v, do = draw_normal(41, [(n, l_q, h, d), (n, l_k, h_kv, d), (n, l_k, h_kv, d),
+                                   (n, l_q, h, d)])
+    scale = 0.09
+    (tq, tk, tv, tdo, o, lse), (dq, dk, dv) = fwd_bwd(q, k, v, do, scale, True, -1, -1, 60)
+    rng = np.random.default_rng(3)
+    init = [rng.standard_normal(s).astype(np.float32)
+            for s in ((n, l_q, h, d), (n, l_k, h_kv, d), (n, l_k, h_kv, d))]
+    acc = [torch.from_numpy(x.copy()).cuda() for x in init]
+    A.attn_bwd_acc(tdo, tq, tk, tv, o, lse, *acc, scale, True, -1, -1, 60, 0)
+    ws = torch.empty(A.bwd_workspace_bytes(n, l_q, l_k, h, h_kv, d), dtype=torch.uint8,
+                     device="cuda")
+    A.attn_bwd_prepare(tdo, o, lse, ws)
+    acc2 = [torch.from_numpy(x.copy()).cuda() for x in init]
+    A.attn_bwd_acc(tdo, tq, tk, tv, o, lse, *acc2, scale, True, -1, -1, 60, 0,
+                   workspace=ws, prepared=True)
+    sq, sk, sv = (torch.empty_like(t) for t in (tq, tk, tv))
+    A.attn_bwd_static(tdo, tq, tk, tv, o, lse, sq, sk, sv, scale, True, -1, -1, 60, 0)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, scale, True, -1, -1, 60, 0)
+    for name, t, x0, r in zip(("dq", "dk", "dv"), acc, init, (rq, rk, rv)):
+        check_grad(host(t) - x0, r, f"accumulated {name}")
+    for a, b in zip(acc, acc2):
+        assert torch.equal(a, b)
+    for g, s in zip((dq, dk, dv), (sq, sk, sv)):
+        assert np.array_equal(g, host(s))
+
+
+@pytest.mark.parametrize("d,h_kv,window", [(64, 1, (-1, -1)), (128, 2, (100, 0))])
+def test_f32_ring_share_backward(d, h_kv, window):
+    """Every rank of a ring of P = 3 (chunks of 100, causal), float32: the
+    fused forward share, then the backward share (prepared once, one
+    accumulating step per chunk); dQ against the rank's rows of the
+    full-sequence gradient, each chunk's (dK, dV) against the rank's
+    contribution to that chunk's keys."""
+    P, c, h = 3, 100, 4
+    L = P * c
+    q, k, v, do = draw_normal(51 + d, [(1, L, h, d), (1, L, h_kv, d), (1, L, h_kv, d),
+                                       (1, L, h, d)])
+    scale = 1.0 / math.sqrt(d)
+    kc = [dev(k[:, s * c:(s + 1) * c], "f32") for s in range(P)]
+    vc = [dev(v[:, s * c:(s + 1) * c], "f32") for s in range(P)]
+    offs = [s * c for s in range(P)]
+    ro, rl = oracle.attention_fwd(q, k, v, scale, True, window[0], window[1])
+    for r in range(P):
+        say(f"[f32 ring bwd] d={d} h_kv={h_kv} window={window} rank {r}")
+        qr, dor = q[:, r * c:(r + 1) * c], do[:, r * c:(r + 1) * c]
+        tq, tdo = dev(qr, "f32"), dev(dor, "f32")
+        out, lse = A.ring_share(tq, kc, vc, offs, r * c, scale, True, fused=True,
+                                window=window)
+        torch.cuda.synchronize()
+        check_o_lse(host(out), host(lse), ro[:, r * c:(r + 1) * c],
+                    rl[:, :, r * c:(r + 1) * c], "f32", f"rank {r} fused share")
+        share = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, scale, True, r * c, window)
+        dq, dk_acc, dv_acc = share.run(kc, vc, offs)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.attention_bwd(qr, k, v, dor, scale, True, window[0], window[1],
+                                          r * c, 0)
+        check_grad(host(dq), rq, f"rank {r} dq")
+        for s in range(P):
+            check_grad(host(dk_acc[s]), rk[:, s * c:(s + 1) * c], f"rank {r} chunk {s} dk")
+            check_grad(host(dv_acc[s]), rv[:, s * c:(s + 1) * c], f"rank {r} chunk {s} dv")
+
+
+@pytest.mark.parametrize("d,causal,window,qo", [
+    (64, False, (-1, -1), 0),
+    (128, True, (-1, -1), 150),
+    (64, True, (30, 0), 0),          # rows whose window misses the chunk
+])
+def test_f32_fused_step(d, causal, window, qo):
+    """attn_fwd_acc (float32) into a random accumulator with a third of its
+    rows empty: equal to the oracle's merge of the accumulator with the
+    oracle's block, every row (kept, replaced, mixed and cleared rows)."""
+    n, l_q, l_k, h, h_kv = 2, 140, 170, 4, 2
+    q, k, v = draw_normal(61 + d, [(n, l_q, h, d), (n, l_k, h_kv, d), (n, l_k, h_kv, d)])
+    scale = 1.0 / math.sqrt(d)
+    ko = 90 if window[0] >= 0 else 0   # the window leaves early rows without keys
+    ro, rl = oracle.attention_fwd(q, k, v, scale, causal, window[0], window[1], qo, ko)
+    rng = np.random.default_rng(d + qo)
+    acc0 = rng.standard_normal((n, l_q, h, d)).astype(np.float32)
+    lse0 = (rng.standard_normal((n, h, l_q)) * 2).astype(np.float32)
+    lse0[rng.random((n, h, l_q)) < 0.33] = -np.inf
+    acc = torch.from_numpy(acc0).cuda()
+    lacc = torch.from_numpy(lse0).cuda()
+    tq, tk, tv = (dev(x, "f32") for x in (q, k, v))
+    A.attn_fwd_acc(tq, tk, tv, acc, lacc, scale, causal, window[0], window[1], qo, ko)
+    torch.cuda.synchronize()
+    mo, ml = oracle.merge(acc0, lse0, ro, rl)
+    assert np.any(np.isneginf(rl)) == (window[0] >= 0)
+    check_o_lse(host(acc), host(lacc), mo, ml, "f32", "fused step")
+    assert A.fwd_kernel_name(n, l_q, l_k, h, h_kv, d, causal, dtype=torch.float32,
+                             fused=True) == f"fwd_f32_kernel<{d}, true>"
+
+
+def test_f32_tiny_workload_forward_and_backward():
+    """The tiny float32 workload at its size (n=1, 128 tokens, 2 heads,
+    d=64, non-causal): forward and backward against the oracle."""
+    w = WORKLOADS["C1"]
+    x = make_inputs(w)
+    do = draw_normal(99, [x["q"].shape])[0]
+    (_, _, _, _, o, lse), (dq, dk, dv) = fwd_bwd(x["q"], x["k"], x["v"], do, w.softmax_scale,
+                                                False)
+    ro, rl = oracle.attention_fwd(x["q"], x["k"], x["v"], w.softmax_scale, False)
+    check_o_lse(host(o), host(lse), ro, rl, "f32", "C1 forward")
+    rq, rk, rv = oracle.attention_bwd(x["q"], x["k"], x["v"], do, w.softmax_scale, False)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
