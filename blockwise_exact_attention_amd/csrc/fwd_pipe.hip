@@ -285,10 +285,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
                                                row0 * kv_row_b, 0, 0);
     };
 
-    // ---- prologue: the wave's Q fragment straight into registers (rows
-    // past the end read as zeros), K and V of the first tile, K of the second.
-    // Lane (col, half) holds row iw + col, dims 16 s + 8 half .. + 7 in qf[s]:
-    // the B operand of the score products, resident for the whole key loop.
+    // ---- prologue: the wave's Q fragment (rows past the end read as
+    // zeros), K and V of the first tile, K of the second.  Lane (col, half)
+    // holds row iw + col, dims 16 s + 8 half .. + 7 in qf[s]: the B operand
+    // of the score products, resident for the whole key loop.  With one key
+    // group it comes straight into registers (each wave reads only its own
+    // rows).
     u32x4_t qf[NDS];
     {
       const long long rows = (long long)p.l_q - i0;
@@ -296,10 +298,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       const uint16_t* base = p.q + ((size_t)b * p.l_q + i0) * q_row + (size_t)hq * D;
       const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0,
                                                         bytes, 0x00020000);
-      const uint32_t off = (uint32_t)(wr * 32 + col) * q_row_b + (uint32_t)half * 16u;
+      if constexpr (KSPLIT == 2) {
+        // both key groups need the same 128 rows: the workgroup loads them
+        // once, whole rows per load, into the second V buffers (first
+        // written by the key loop's first step) in the tiles' swizzled
+        // layout; every wave reads its fragment back after the barrier
+        constexpr int QLOADS = QROWS / RPD / kWaves;
+        static_assert(QLOADS >= 1 && QROWS * RB == KSPLIT * TILE, "Q staging");
+        const uint32_t q_voff =
+            lrow * q_row_b + ((lchunk ^ chunk_swz<D>((uint32_t)wave_all * RPD + lrow)) * 16u);
 #pragma unroll
-      for (int s = 0; s < NDS; ++s)
-        qf[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 32u * s), 0, 0);
+        for (int x = 0; x < QLOADS; ++x) {
+          const uint32_t row0 = (uint32_t)((x * kWaves + wave_all) * RPD);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(&v_lds1[0][0] + row0 * RB),
+                                                   16, q_voff, row0 * q_row_b, 0, 0);
+        }
+      } else {
+        const uint32_t off = (uint32_t)(wr * 32 + col) * q_row_b + (uint32_t)half * 16u;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s)
+          qf[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 32u * s), 0, 0);
+      }
     }
     // cursors of this group's first tile, of the tile whose V (and mask) the
     // first step needs, and of the tile whose K it loads
@@ -317,6 +336,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
+    if constexpr (KSPLIT == 2) {
+#pragma unroll
+      for (int s = 0; s < NDS; ++s)
+        qf[s] = *reinterpret_cast<const u32x4_t*>(&v_lds1[0][0] + (uint32_t)wr * 32u * RB +
+                                                  (ka0 ^ (32u * s)));
+    }
 
     // The sign of the scale is folded into Q (sign-bit flip, exact) and a
     // zero scale becomes Q = 0 with c = log2(e) (every allowed score is then
