@@ -1,7 +1,7 @@
 """Benchmark of the blockwise exact-attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--no-extras] [--no-cpu]
-    python bench.py --workload {c3-steps,c3-fused,c3-share,c3-bwd,c3-bwd-one,c4,c5-fwd,c5-bwd}
+    python bench.py --workload {c3-steps,c3-fused,c3-share,c3-bwd,c3-bwd-one,c4,c5-fwd,c5-bwd,mqa-c2,mqa-c5}
 
 Workload: causal multi-head attention, n=2, l=2048, h=h_kv=16, d=128, bf16,
 scale 1/sqrt(128), synthetic N(0,1) inputs resident in HBM.  A step is one
@@ -51,6 +51,7 @@ def parse():
                     help="only the headline workload (and the CPU baseline)")
     ap.add_argument("--workload", default="c2",
                     choices=("c2", "c3-steps", "c3-fused", "c3-share", "c3-bwd", "c3-bwd-one",
+                             "mqa-c2", "mqa-c5",
                              "c4", "c5-fwd", "c5-bwd"),
                     help="time only this workload's call (for profiler runs); c2 "
                          "is the default full run")
@@ -529,6 +530,20 @@ def single_workload(name, A, torch, allowed_pairs, fwd_flops, bwd_flops, WORKLOA
         return (lambda: A.attn_bwd(tdo, tq, tk, tv, o, lse, dq, dk, dv, w.softmax_scale,
                                    True, workspace=ws), bwd_flops(w.n, w.h, w.d, pairs),
                 "16k-token causal backward")
+    if name.startswith("mqa"):
+        # the headline and 16k-token causal forwards with one key/value head
+        # (multi-query): the first K/V head of the same inputs
+        w = WORKLOADS["C2" if name == "mqa-c2" else "C5"]
+        x = make_inputs(w)
+        tq = t(x["q"])
+        tk = t(np.ascontiguousarray(x["k"][:, :, :1]))
+        tv = t(np.ascontiguousarray(x["v"][:, :, :1]))
+        o = torch.empty_like(tq)
+        lse = torch.empty((w.n, w.h, w.l_q), dtype=torch.float32, device=dev)
+        pairs = allowed_pairs(w.l_q, w.l_k, True)
+        return (lambda: A.attn_fwd(tq, tk, tv, o, lse, w.softmax_scale, True),
+                fwd_flops(w.n, w.h, w.d, pairs),
+                f"causal MQA forward n={w.n} l={w.l_q} h={w.h} h_kv=1 d={w.d}")
     raise ValueError(f"unknown workload {name}")
 
 
@@ -612,10 +627,11 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
     del bshare, tdo, kf, vf, ag_out, ag_lse, share, kc, vc, tq
 
     for key, name in (("window_256", "c4"), ("long_16k_fwd", "c5-fwd"),
-                      ("long_16k_bwd", "c5-bwd")):
+                      ("long_16k_bwd", "c5-bwd"), ("mqa_c2", "mqa-c2"),
+                      ("mqa_16k_fwd", "mqa-c5")):
         fn, flops, what = single_workload(name, A, torch, allowed_pairs, fwd_flops,
                                           bwd_flops, WORKLOADS, make_inputs)
-        n_steps = steps if name == "c4" else max(5, steps // 8)
+        n_steps = steps if name in ("c4", "mqa-c2") else max(5, steps // 8)
         ms = timed(fn, n_steps, 3, torch)
         r = {"what": what, "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
              "frac": _frac(flops / (ms * 1e-3) / 1e12)}
@@ -623,6 +639,10 @@ def extras(A, torch, args, allowed_pairs, fwd_flops, bwd_flops, merge_bytes,
             r["kernel"] = A.fwd_kernel_name(4, 4096, 4096, 16, 16, 64, True, 256, 0)
         if name == "c5-fwd":
             r["kernel"] = A.fwd_kernel_name(1, 16384, 16384, 16, 16, 128, True)
+        if name == "mqa-c2":
+            r["kernel"] = A.fwd_kernel_name(2, 2048, 2048, 16, 1, 128, True)
+        if name == "mqa-c5":
+            r["kernel"] = A.fwd_kernel_name(1, 16384, 16384, 16, 1, 128, True)
         res[key] = r
         del fn
         torch.cuda.empty_cache()
