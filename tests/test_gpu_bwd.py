@@ -133,11 +133,17 @@ def test_c5_backward_full():
         check_grad(dv, rv, f"C5 head {g} dv")
 
 
-def test_fp32_backward_is_rejected():
+def test_fp32_one_launch_ring_backward_is_rejected():
+    """The float32 backward runs per step (tests/test_gpu_f32.py); the
+    three-launch ring share is bf16 only and refuses float32 before any
+    launch."""
     q = torch.zeros((1, 64, 2, 64), device="cuda")
     lse = torch.zeros((1, 2, 64), device="cuda")
-    with pytest.raises(A.AttnError if hasattr(A, "AttnError") else Exception):
-        A.attention_backward(q, q, q, q, q, lse)
+    kc = [torch.zeros((1, 32, 1, 64), device="cuda")]
+    acc = [torch.zeros((1, 32, 1, 64), device="cuda")]
+    with pytest.raises(Exception):
+        A.attn_bwd_ring(q, q, q, lse, kc, kc, [0], acc, [a.clone() for a in acc],
+                        torch.empty_like(q), 0.1, True)
 
 
 @pytest.mark.parametrize("d,h_kv,window,fused,one_launch", [
