@@ -303,17 +303,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p, int 
                       ((long long)(kw + kKeysPerWave - 1) - i0 <= dhi_);
     uint32_t ka = ka0;
     asm volatile("" : "+v"(ka));
-    // S = Q K^T and dP = dO V^T: [32 queries x 32 keys] blocks, lane = key
+    // S = Q K^T and dP = dO V^T: [32 queries x 32 keys] blocks, lane = key.
+    // The Q and dO operands are read from LDS AH1 product pairs ahead (with
+    // one wave per SIMD nothing else covers the read latency), the query
+    // blocks interleaved so that four accumulations are in flight.
     f32x16_t sa[NQB], dpa[NQB];
+    {
+      constexpr int AH1 = 3;
+      constexpr int NX1 = NQB * NDS;
+      u32x4_t ra[AH1 + 1], rb[AH1 + 1];
+      auto rd1 = [&](int x) {
+        const int s = x / NQB, qb = x % NQB;
+        ra[x % (AH1 + 1)] =
+            *reinterpret_cast<const u32x4_t*>(ql + qb * 32 * RB + (ka ^ (32u * s)));
+        rb[x % (AH1 + 1)] =
+            *reinterpret_cast<const u32x4_t*>(ol + qb * 32 * RB + (ka ^ (32u * s)));
+      };
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+      for (int x = 0; x < AH1; ++x) rd1(x);
 #pragma unroll
-      for (int s = 0; s < NDS; ++s) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ql + qb * 32 * RB + (ka ^ (32u * s)));
-        sa[qb] = mfma32x32x16(a, kf[s], s == 0 ? f32x16_t{} : sa[qb]);
-        const u32x4_t a2 = *reinterpret_cast<const u32x4_t*>(ol + qb * 32 * RB + (ka ^ (32u * s)));
-        dpa[qb] = mfma32x32x16(a2, vf[s], s == 0 ? f32x16_t{} : dpa[qb]);
+      for (int x = 0; x < NX1; ++x) {
+        if (x + AH1 < NX1) rd1(x + AH1);
+        const int s = x / NQB, qb = x % NQB;
+        sa[qb] = mfma32x32x16(ra[x % (AH1 + 1)], kf[s], s == 0 ? f32x16_t{} : sa[qb]);
+        dpa[qb] = mfma32x32x16(rb[x % (AH1 + 1)], vf[s], s == 0 ? f32x16_t{} : dpa[qb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
     if (!full) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
