@@ -13,6 +13,7 @@ import shutil
 import subprocess
 import sys
 import concurrent.futures as cf
+import ctypes
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -63,6 +64,13 @@ def build(verbose=True):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every symbol must resolve (a kernel whose host launch stub the compiler
+    # failed to emit links, but leaves an undefined symbol behind)
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"libattn.so does not load: {e}") from None
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
