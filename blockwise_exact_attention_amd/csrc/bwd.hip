@@ -89,7 +89,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
   constexpr int TPR = D / 8;  // threads per row
   const long long rows = (long long)p.n * p.l_q * p.h;
-  const long long row = ((long long)blockIdx.x * kThreads + threadIdx.x) / TPR;
+  // a capped grid walks the blocks (one pass on every realistic shape)
+  const long long nblocks = (rows * TPR + kThreads - 1) / kThreads;
+  for (long long vb = blockIdx.x; vb < nblocks; vb += gridDim.x) {
+  const long long row = (vb * kThreads + threadIdx.x) / TPR;
   const int part = threadIdx.x % TPR;
   float acc = 0.f;
   const bool ok = row < rows;
@@ -115,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
     p.dd[li] = acc;
     const float l = p.lse[li];
     p.lse2[li] = (l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
+  }
   }
 }
 
@@ -877,7 +881,7 @@ template <int D>
 void launch_pre_d(const BwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.n * p.l_q * p.h;
   const long long pre_blocks = (rows * (D / 8) + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(kThreads),
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(capped_grid(pre_blocks)), dim3(kThreads),
                      0, stream, p);
 }
 

@@ -70,7 +70,10 @@ template <int D>
 __global__ __launch_bounds__(kF32BwdThreads) void bwd_f32_pre_kernel(BwdF32Params p) {
   constexpr int TPR = D / 4;  // threads per row, one 16-byte chunk each
   const long long rows = (long long)p.n * p.l_q * p.h;
-  const long long row = ((long long)blockIdx.x * kF32BwdThreads + threadIdx.x) / TPR;
+  // a capped grid walks the blocks (one pass on every realistic shape)
+  const long long nblocks = (rows * TPR + kF32BwdThreads - 1) / kF32BwdThreads;
+  for (long long vb = blockIdx.x; vb < nblocks; vb += gridDim.x) {
+  const long long row = (vb * kF32BwdThreads + threadIdx.x) / TPR;
   const int part = threadIdx.x % TPR;
   const bool ok = row < rows;
   const long long rr = ok ? row : rows - 1;
@@ -92,6 +95,7 @@ __global__ __launch_bounds__(kF32BwdThreads) void bwd_f32_pre_kernel(BwdF32Param
     p.dd[li] = acc;
     const float l = p.lse[li];
     p.lse2[li] = (l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
+  }
   }
 }
 
@@ -287,7 +291,7 @@ template <int D>
 void launch_f32_pre_d(const BwdF32Params& p, hipStream_t stream) {
   const long long rows = (long long)p.n * p.l_q * p.h;
   const long long blocks = (rows * (D / 4) + kF32BwdThreads - 1) / kF32BwdThreads;
-  hipLaunchKernelGGL((bwd_f32_pre_kernel<D>), dim3((unsigned)blocks), dim3(kF32BwdThreads), 0,
+  hipLaunchKernelGGL((bwd_f32_pre_kernel<D>), dim3(capped_grid(blocks)), dim3(kF32BwdThreads), 0,
                      stream, p);
 }
 

@@ -53,6 +53,10 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v,
                           hipStream_t stream, float* acc = nullptr,
                           float* lse_acc = nullptr);
 
+// A launch grid of min(blocks, 2^20) blocks (at least 1) for the kernels
+// that walk their blocks in several passes when there are more.
+unsigned capped_grid(long long blocks);
+
 hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
                         const float* lse_blk, int n, int l, int h, int d,
                         bool blk_bf16, hipStream_t stream);

@@ -10,6 +10,8 @@
 // update_out_and_lse - the same merge in sigmoid form, and the first block
 // simply becomes the accumulator (here: whenever the accumulator's LSE is
 // -inf).
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -64,19 +66,14 @@ __device__ __forceinline__ void merge_row_weights(float* __restrict__ lse_acc,
 // memory round trip, not two.  The O data is touched once per merge: its
 // loads and stores carry the nontemporal hint (streamed past the caches;
 // measured on gfx950 from HBM: 11.3 -> 9.6 us for a 42 MB merge).
+// One block of the vector path: rows i0 .. i0 + R - 1 of (batch b, head hq),
+// bh = b * h + hq.
 template <bool BLK_BF16>
-__global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
-    float* __restrict__ acc, float* __restrict__ lse_acc,
-    const void* __restrict__ blk, const float* __restrict__ lse_blk, int l,
-    int h, int d, int iblocks) {
-  __shared__ float s_wa[kMergeMaxRows];
-  __shared__ float s_wb[kMergeMaxRows];
-  __shared__ int s_mode[kMergeMaxRows];
+__device__ __forceinline__ void merge_vec_block(
+    float* __restrict__ acc, float* __restrict__ lse_acc, const void* __restrict__ blk,
+    const float* __restrict__ lse_blk, int l, int h, int d, size_t bh, size_t b, int hq,
+    int i0, float* s_wa, float* s_wb, int* s_mode) {
   const int R = kMergeElems / d;
-  const int bh = blockIdx.x / iblocks;       // b * h + hq
-  const int i0 = (blockIdx.x - bh * iblocks) * R;
-  const int b = bh / h;
-  const int hq = bh - b * h;
   const int nr = min(R, l - i0);
   const int tid = threadIdx.x;
   const size_t row_stride = (size_t)h * d;
@@ -150,17 +147,49 @@ __global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
   }
 }
 
+// WALK: the grid is capped and walks the blocks in several passes (shapes
+// beyond 2^20 blocks); otherwise every block merges its own rows once.
+template <bool BLK_BF16, bool WALK>
+__global__ __launch_bounds__(kMergeThreads) void merge_vec_kernel(
+    float* __restrict__ acc, float* __restrict__ lse_acc,
+    const void* __restrict__ blk, const float* __restrict__ lse_blk, int l,
+    int h, int d, int iblocks, long long nblocks) {
+  __shared__ float s_wa[kMergeMaxRows];
+  __shared__ float s_wb[kMergeMaxRows];
+  __shared__ int s_mode[kMergeMaxRows];
+  const int R = kMergeElems / d;
+  if (!WALK) {
+    const int bh = blockIdx.x / iblocks;       // b * h + hq
+    const int i0 = (blockIdx.x - bh * iblocks) * R;
+    const int b = bh / h;
+    const int hq = bh - b * h;
+    merge_vec_block<BLK_BF16>(acc, lse_acc, blk, lse_blk, l, h, d, (size_t)bh, (size_t)b, hq,
+                              i0, s_wa, s_wb, s_mode);
+    return;
+  }
+  for (long long vb = blockIdx.x; vb < nblocks; vb += gridDim.x) {
+    const long long bh = vb / iblocks;
+    const int i0 = (int)(vb - bh * iblocks) * R;
+    const long long b = bh / h;
+    const int hq = (int)(bh - b * h);
+    merge_vec_block<BLK_BF16>(acc, lse_acc, blk, lse_blk, l, h, d, (size_t)bh, (size_t)b, hq,
+                              i0, s_wa, s_wb, s_mode);
+    __syncthreads();   // the next block's weights overwrite s_mode, s_wa, s_wb
+  }
+}
+
 // Scalar path for any other d: a block covers up to 1024 / d rows.
 template <bool BLK_BF16>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     float* __restrict__ acc, float* __restrict__ lse_acc,
     const void* __restrict__ blk, const float* __restrict__ lse_blk, int l,
-    int h, int d, long long rows_total, int rows_per_block) {
+    int h, int d, long long rows_total, int rows_per_block, long long nblocks) {
   __shared__ float s_wa[kMergeMaxRows];
   __shared__ float s_wb[kMergeMaxRows];
   __shared__ int s_mode[kMergeMaxRows];
 
-  const long long r0 = (long long)blockIdx.x * rows_per_block;
+  for (long long vb = blockIdx.x; vb < nblocks; vb += gridDim.x) {
+  const long long r0 = vb * rows_per_block;
   const int nr = (int)min((long long)rows_per_block, rows_total - r0);
   const int tid = threadIdx.x;
   if (tid < nr) {
@@ -188,6 +217,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
         : static_cast<const float*>(blk)[e0 + e];
     acc[e0 + e] = (mode == 1) ? bv : acc[e0 + e] * s_wa[rr] + bv * s_wb[rr];
   }
+  __syncthreads();
+  }
 }
 
 // Merge of an empty block (every row's LSE -inf, e.g. a chunk with no keys)
@@ -198,7 +229,7 @@ __global__ __launch_bounds__(256) void acc_clear_empty_kernel(float* __restrict_
                                                               int l, int h, int d,
                                                               long long rows) {
   __shared__ int s_clear[256];
-  const long long r0 = (long long)blockIdx.x * 256;
+  for (long long r0 = (long long)blockIdx.x * 256; r0 < rows; r0 += (long long)gridDim.x * 256) {
   const int nr = (int)min(256LL, rows - r0);
   const int tid = threadIdx.x;
   if (tid < nr) {
@@ -214,6 +245,8 @@ __global__ __launch_bounds__(256) void acc_clear_empty_kernel(float* __restrict_
   const int ne = nr * d;
   for (int e = tid; e < ne; e += 256)
     if (s_clear[e / d]) acc[e0 + e] = 0.f;
+  __syncthreads();
+  }
 }
 
 // 16-byte stores where the accumulator is 16-byte aligned (n4 = n_acc / 4),
@@ -266,9 +299,20 @@ __global__ __launch_bounds__(256) void acc_cast_kernel(const float* __restrict__
 __global__ __launch_bounds__(256) void hbm_copy_kernel(const f32x4_t* __restrict__ src,
                                                        f32x4_t* __restrict__ dst,
                                                        long long n4) {
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(src + e), dst + e);
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n4;
+       e += (long long)gridDim.x * 256)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + e), dst + e);
 }
+
+}  // namespace
+
+// A grid of at most 2^20 blocks: launches count work-items in 32 bits, so the
+// elementwise kernels walk larger block counts in several passes.
+unsigned capped_grid(long long blocks) {
+  return (unsigned)std::max(1LL, std::min(blocks, 1LL << 20));
+}
+
+namespace {
 
 unsigned grid_for(long long work, int per_block) {
   long long g = (work + per_block - 1) / per_block;
@@ -287,31 +331,41 @@ hipError_t launch_merge(float* out_acc, float* lse_acc, const void* out_blk,
       kMergeElems / d <= kMergeMaxRows) {
     const int rpb = kMergeElems / d;
     const int iblocks = (l + rpb - 1) / rpb;
-    dim3 grid((unsigned)((long long)n * h * iblocks)), block(kMergeThreads);
-    if (blk_bf16)
-      hipLaunchKernelGGL((merge_vec_kernel<true>), grid, block, 0, stream, out_acc,
-                         lse_acc, out_blk, lse_blk, l, h, d, iblocks);
-    else
-      hipLaunchKernelGGL((merge_vec_kernel<false>), grid, block, 0, stream, out_acc,
-                         lse_acc, out_blk, lse_blk, l, h, d, iblocks);
+    const long long nblocks = (long long)n * h * iblocks;
+    dim3 grid(capped_grid(nblocks)), block(kMergeThreads);
+    const bool walk = nblocks > (long long)grid.x;
+    if (blk_bf16) {
+      if (walk)
+        hipLaunchKernelGGL((merge_vec_kernel<true, true>), grid, block, 0, stream, out_acc,
+                           lse_acc, out_blk, lse_blk, l, h, d, iblocks, nblocks);
+      else
+        hipLaunchKernelGGL((merge_vec_kernel<true, false>), grid, block, 0, stream, out_acc,
+                           lse_acc, out_blk, lse_blk, l, h, d, iblocks, nblocks);
+    } else if (walk) {
+      hipLaunchKernelGGL((merge_vec_kernel<false, true>), grid, block, 0, stream, out_acc,
+                         lse_acc, out_blk, lse_blk, l, h, d, iblocks, nblocks);
+    } else {
+      hipLaunchKernelGGL((merge_vec_kernel<false, false>), grid, block, 0, stream, out_acc,
+                         lse_acc, out_blk, lse_blk, l, h, d, iblocks, nblocks);
+    }
     return hipGetLastError();
   }
   int rpb = 1024 / d;
   if (rpb < 1) rpb = 1;
   if (rpb > kMergeMaxRows) rpb = kMergeMaxRows;
   const long long blocks = (rows + rpb - 1) / rpb;
-  dim3 grid((unsigned)blocks), block(kMergeThreads);
+  dim3 grid(capped_grid(blocks)), block(kMergeThreads);
   if (blk_bf16)
     hipLaunchKernelGGL((merge_kernel<true>), grid, block, 0, stream, out_acc,
-                       lse_acc, out_blk, lse_blk, l, h, d, rows, rpb);
+                       lse_acc, out_blk, lse_blk, l, h, d, rows, rpb, blocks);
   else
     hipLaunchKernelGGL((merge_kernel<false>), grid, block, 0, stream, out_acc,
-                       lse_acc, out_blk, lse_blk, l, h, d, rows, rpb);
+                       lse_acc, out_blk, lse_blk, l, h, d, rows, rpb, blocks);
   return hipGetLastError();
 }
 
 hipError_t launch_hbm_copy(const void* src, void* dst, long long n4, hipStream_t stream) {
-  hipLaunchKernelGGL(hbm_copy_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(hbm_copy_kernel, dim3(capped_grid((n4 + 255) / 256)), dim3(256), 0, stream,
                      static_cast<const f32x4_t*>(src), static_cast<f32x4_t*>(dst), n4);
   return hipGetLastError();
 }
@@ -319,7 +373,7 @@ hipError_t launch_hbm_copy(const void* src, void* dst, long long n4, hipStream_t
 hipError_t launch_acc_clear_empty(float* out_acc, const float* lse_acc, int n, int l,
                                   int h, int d, hipStream_t stream) {
   const long long rows = (long long)n * l * h;
-  hipLaunchKernelGGL(acc_clear_empty_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL(acc_clear_empty_kernel, dim3(capped_grid((rows + 255) / 256)), dim3(256),
                      0, stream, out_acc, lse_acc, l, h, d, rows);
   return hipGetLastError();
 }
