@@ -86,8 +86,11 @@ int check_attn_args(int n, int l_q, int l_k, int h, int h_kv, int d,
   // a 32-bit launch
   if ((long long)((l_q + 63) / 64) * n * h > INT_MAX) return ATTN_ERR_SHAPE;
   if ((long long)((l_k + 63) / 64) * n * h_kv * 4 > INT_MAX) return ATTN_ERR_SHAPE;
-  // the backward's row pass launches one workgroup per 16 query rows
-  if ((long long)n * l_q * h > 16LL * INT_MAX) return ATTN_ERR_SHAPE;
+  // the attention kernels launch up to four work-items per query row and
+  // per key row, and a launch counts its work-items in 32 bits (the row
+  // passes and elementwise kernels walk capped grids instead)
+  if ((long long)n * l_q * h * 4 > (long long)UINT_MAX) return ATTN_ERR_SHAPE;
+  if ((long long)n * l_k * h_kv * 4 > (long long)UINT_MAX) return ATTN_ERR_SHAPE;
   // the kernels address a 64-row tile with 32-bit offsets from its first
   // row: a row (h or h_kv heads of d float32 values at most) must stay
   // below 32 MiB

@@ -73,9 +73,11 @@ enum attn_status {
   ATTN_ERR_NULL = 1,        /* a pointer to a non-empty tensor is NULL           */
   ATTN_ERR_SHAPE = 2,       /* a size is negative, h, h_kv or d is 0,
                                h % h_kv != 0, sizes overflow, a row of q
-                               (h * d) exceeds 32 MiB in float32, a grid
-                               would exceed 2^31 workgroups, or a chunk count
-                               outside 1..ATTN_RING_MAX_CHUNKS                   */
+                               (h * d) exceeds 32 MiB in float32, a launch
+                               would exceed 2^31 workgroups or 2^32 work-items
+                               (n*l_q*h >= 2^30 query rows or n*l_k*h_kv >= 2^30
+                               key rows), or a chunk count outside
+                               1..ATTN_RING_MAX_CHUNKS                           */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite
                                scale, or fp32 one-launch ring share (forward
                                or backward)                                      */

@@ -172,7 +172,11 @@ def test_fwd_null(field):
                                 dict(d=0), dict(n=1 << 30, l_q=1 << 30),
                                 dict(h=1 << 18, h_kv=1 << 18),
                                 dict(n=1 << 20, l_q=64, l_k=1 << 20, h=64, h_kv=64),
-                                dict(n=1 << 20, l_q=64, l_k=64, h=1 << 10, h_kv=1)])
+                                dict(n=1 << 20, l_q=64, l_k=64, h=1 << 10, h_kv=1),
+                                # 2^30 query rows (2^32 work-items at four per row)
+                                dict(n=1, l_q=1 << 30, l_k=64, h=1, h_kv=1),
+                                # 2^30 key rows (2^32 work-items at four per row)
+                                dict(n=1, l_q=64, l_k=1 << 30, h=1, h_kv=1)])
 def test_fwd_shape(kw):
     assert _fwd(**kw) == ATTN_ERR_SHAPE
 
