@@ -519,8 +519,8 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void fwd_bf
           const uint32_t c = (ln % CPR) ^ chunk_swz<D>((uint32_t)r);
           const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stage + r * RB + c * 16);
           if (iw + r <= last_row)
-            *reinterpret_cast<u32x4_t*>(p.o + ((size_t)b * p.l_q + iw + r) * q_row +
-                                        (size_t)hq * D + 8 * (ln % CPR)) = val;
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(
+                p.o + ((size_t)b * p.l_q + iw + r) * q_row + (size_t)hq * D + 8 * (ln % CPR)));
         }
         if (half == 0 && qi <= last_row) {
           const float muse = (m == kNegInf) ? 0.f : m;

@@ -872,7 +872,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
       for (int x = 0; x < NST; ++x) {
         const uint32_t r = (uint32_t)(x * RPI) + eln / CPH;
         if (iw + (int)r <= last_row)
-          *reinterpret_cast<u32x4_t*>(obase + (size_t)r * q_row + 8 * c) = val[x];
+          __builtin_nontemporal_store(val[x],
+                                      reinterpret_cast<u32x4_t*>(obase + (size_t)r * q_row + 8 * c));
       }
       if (grp == 0 && ehalf == 0 && eqi <= last_row) p.lse[(size_t)head * p.l_q + eqi] = lse_b;
     }
