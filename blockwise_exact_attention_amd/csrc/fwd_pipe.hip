@@ -326,9 +326,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_pipe_kernel(PipeParams p) {
     Cur curV = cur_next(cur0);
     Cur curK = cur_next(curV);
     // only Q and the first K tile before the first scores: V of the first
-    // tile and K of the second are loaded between those products (the
-    // prologue's loads are bound by the CU's load rate, so this hides the
-    // first tile's compute behind them)
+    // tile and K of the second are loaded between those products, so that
+    // their latency hides behind the first tile's compute
     if (n_g > 0) {
       const auto rk = kv_rsrc(cur0, false);
 #pragma unroll

@@ -165,8 +165,8 @@ def test_ring_without_any_key():
     (128, 2, 2, True, (6000, 0)),
 ])
 def test_pipelined_kernel_on_long_chunks(d, h, h_kv, causal, window):
-    """Key loops long enough (64 and more key tiles per q tile on average)
-    that attn_fwd and the fused step run the pipelined kernel: its plain and
+    """Key loops long enough (12 and more key tiles per 128-row q tile on
+    average) that attn_fwd and the fused step run the pipelined kernel: its plain and
     accumulating epilogues against the oracle, ragged lengths, and the
     one-chunk share (always the pipelined kernel) bit-equal to attn_fwd."""
     l_q, l_k = 333, 9001
