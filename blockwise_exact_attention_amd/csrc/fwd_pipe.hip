@@ -38,8 +38,10 @@
 //    window edges, ragged ends) get a mask pass before phase 2.
 //  * K and V tiles of 64 keys are double-buffered in LDS and filled by
 //    direct buffer-to-LDS loads; K runs one tile ahead of V.  One barrier
-//    per tile.  Each wave loads its Q rows straight into registers at the
-//    start of a q tile, beside the first K/V loads.
+//    per tile.  KSPLIT = 2: the workgroup stages the q tile's rows in LDS
+//    once (both key groups need them) and every wave reads its fragment
+//    from there; KSPLIT = 1: each wave loads its own rows straight into
+//    registers.
 //  * The running max is updated lazily (rescale only when a tile's max
 //    exceeds it by a slack), so O is rarely touched outside the products.
 //  * Normalised O leaves through LDS as row-contiguous stores.  The ACC
