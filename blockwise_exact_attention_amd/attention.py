@@ -445,8 +445,9 @@ class RingShare:
     that chunk's absolute offset) either attn_fwd + attn_merge or, with
     fused=True, the single attn_fwd_acc step, then the final cast - all on
     one stream, nothing synchronised (flash_sharding.py, ring_fwd).  With
-    one_launch=True (bf16, at most ATTN_RING_MAX_CHUNKS chunks) the whole
-    share is the single attn_fwd_ring launch instead, writing the final O and
+    one_launch=True (at most ATTN_RING_MAX_CHUNKS chunks) the whole share is
+    the attn_fwd_ring call instead (one launch for bf16; float32 merges one
+    fused step per chunk into the output itself), writing the final O and
     LSE directly."""
 
     def __init__(self, q, scale, causal, q_offset, window=(-1, -1)):

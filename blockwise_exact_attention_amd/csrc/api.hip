@@ -219,15 +219,15 @@ int attn_fwd_ring(const void* q, const void* const* k_chunks, const void* const*
     const int st = check_attn_args(n, l_q, l_k_chunks[c], h, h_kv, d, scale, dtype);
     if (st != ATTN_OK) return st;
   }
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  const long long qb = (long long)n * l_q * h * d * 2;
+  const long long es = dtype == ATTN_F32 ? 4 : 2;
+  const long long qb = (long long)n * l_q * h * d * es;
   const long long lb = (long long)n * h * l_q * 4;
   if (missing(q, qb) || missing(out, qb) || missing(lse, lb)) return ATTN_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_ERR_ALIGN;
   const Range rq = range(q, qb), ro = range(out, qb), rl = range(lse, lb);
   if (overlap(ro, rq) || overlap(rl, rq) || overlap(rl, ro)) return ATTN_ERR_ALIAS;
   for (int c = 0; c < n_chunks; ++c) {
-    const long long kb = (long long)n * l_k_chunks[c] * h_kv * d * 2;
+    const long long kb = (long long)n * l_k_chunks[c] * h_kv * d * es;
     if (missing(k_chunks[c], kb) || missing(v_chunks[c], kb)) return ATTN_ERR_NULL;
     if (!aligned(k_chunks[c], 16) || !aligned(v_chunks[c], 16)) return ATTN_ERR_ALIGN;
     const Range rk = range(k_chunks[c], kb), rv = range(v_chunks[c], kb);
@@ -238,6 +238,19 @@ int attn_fwd_ring(const void* q, const void* const* k_chunks, const void* const*
 
   (void)hipGetLastError();
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_F32) {
+    // float32: out and lse are the accumulator itself (O = 0, LSE = -inf),
+    // into which one fused step per chunk with keys merges its block
+    hipError_t e = bea::launch_acc_init(static_cast<float*>(out), lse, n, l_q, h, d, hs);
+    for (int c = 0; c < n_chunks && e == hipSuccess; ++c) {
+      if ((long long)n * l_k_chunks[c] == 0) continue;
+      AttnShape sc{n, l_q, l_k_chunks[c], h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+      mask_bounds(causal, win_l, win_r, q_offset, k_offsets[c], &sc.dlo, &sc.dhi);
+      e = bea::launch_fwd_f32(q, k_chunks[c], v_chunks[c], nullptr, nullptr, sc, hs,
+                              static_cast<float*>(out), lse);
+    }
+    return finish(e);
+  }
   // chunks without keys add nothing: drop them
   bea::FwdChunk ch[bea::kMaxChunks];
   int m = 0;
@@ -542,7 +555,7 @@ int attn_bwd_ring(const void* dout, const void* q, const void* out, const float*
     const int st = check_attn_args(n, l_q, l_k_chunks[c], h, h_kv, d, scale, dtype);
     if (st != ATTN_OK) return st;
   }
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const long long es = dtype == ATTN_F32 ? 4 : 2;
   const long long qe = (long long)n * l_q * h * d;
   const long long lb = (long long)n * h * l_q * 4;
   if (missing(dout, qe) || missing(q, qe) || missing(out, qe) || missing(lse, lb) ||
@@ -570,16 +583,16 @@ int attn_bwd_ring(const void* dout, const void* q, const void* out, const float*
   // each other
   Range ins[4 + 2 * ATTN_RING_MAX_CHUNKS], outs[2 + 2 * ATTN_RING_MAX_CHUNKS];
   int ni = 0, no = 0;
-  ins[ni++] = range(dout, qe * 2);
-  ins[ni++] = range(q, qe * 2);
-  ins[ni++] = range(out, qe * 2);
+  ins[ni++] = range(dout, qe * es);
+  ins[ni++] = range(q, qe * es);
+  ins[ni++] = range(out, qe * es);
   ins[ni++] = range(lse, lb);
-  outs[no++] = range(dq, qe * 2);
+  outs[no++] = range(dq, qe * es);
   outs[no++] = range(workspace, (long long)need);
   for (int c = 0; c < n_chunks; ++c) {
     const long long ke = (long long)n * l_k_chunks[c] * h_kv * d;
-    ins[ni++] = range(k_chunks[c], ke * 2);
-    ins[ni++] = range(v_chunks[c], ke * 2);
+    ins[ni++] = range(k_chunks[c], ke * es);
+    ins[ni++] = range(v_chunks[c], ke * es);
     outs[no++] = range(dk_acc_chunks[c], ke * 4);
     outs[no++] = range(dv_acc_chunks[c], ke * 4);
   }
@@ -594,7 +607,24 @@ int attn_bwd_ring(const void* dout, const void* q, const void* out, const float*
   hipStream_t hs = static_cast<hipStream_t>(stream);
   // no keys in any chunk: dQ = 0 (as 32-bit words), nothing added
   if (!any_keys)
-    return finish(bea::launch_acc_init(static_cast<float*>(dq), nullptr, n, l_q, h, d / 2, hs));
+    return finish(bea::launch_acc_init(static_cast<float*>(dq), nullptr, n, l_q, h,
+                                       dtype == ATTN_F32 ? d : d / 2, hs));
+  if (dtype == ATTN_F32) {
+    // float32: dq is its own accumulator (cleared first); D and the base-2
+    // LSE prepared once, then one accumulating backward per chunk with keys
+    float* dqf = static_cast<float*>(dq);
+    hipError_t e = bea::launch_acc_init(dqf, nullptr, n, l_q, h, d, hs);
+    if (e == hipSuccess)
+      e = bea::launch_bwd_f32_prepare(dout, out, lse, n, l_q, h, d, workspace, hs);
+    for (int c = 0; c < n_chunks && e == hipSuccess; ++c) {
+      if ((long long)n * l_k_chunks[c] == 0) continue;
+      AttnShape sc{n, l_q, l_k_chunks[c], h, h_kv, d, scale, 0, 0, causal ? 1 : 0};
+      mask_bounds(causal, win_l, win_r, q_offset, k_offsets[c], &sc.dlo, &sc.dhi);
+      e = bea::launch_bwd_f32(dout, q, k_chunks[c], v_chunks[c], out, lse, dqf,
+                              dk_acc_chunks[c], dv_acc_chunks[c], sc, workspace, true, true, hs);
+    }
+    return finish(e);
+  }
   bea::BwdChunkArgs ch[bea::kMaxChunks];
   int m = 0;
   for (int c = 0; c < n_chunks; ++c) {

@@ -78,9 +78,8 @@ enum attn_status {
                                (n*l_q*h >= 2^30 query rows or n*l_k*h_kv >= 2^30
                                key rows), or a chunk count outside
                                1..ATTN_RING_MAX_CHUNKS                           */
-  ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, non-finite
-                               scale, or fp32 one-launch ring share (forward
-                               or backward)                                      */
+  ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype or non-finite
+                               scale                                             */
   ATTN_ERR_HIP = 4,         /* the HIP runtime reported a launch failure         */
   ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than required (or NULL when
                                required)                                         */
@@ -181,19 +180,22 @@ const char* attn_fwd_kernel_name(int n, int l_q, int l_k, int h, int h_kv, int d
  * k_offsets[c] + j (what attn_acc_init, attn_fwd_acc per chunk and
  * attn_acc_cast give, up to rounding order).
  *
- *   q            [n,l_q,h,d]     in   bfloat16 (dtype must be ATTN_BF16)
+ *   q            [n,l_q,h,d]     in   dtype
  *   k_chunks[c], v_chunks[c]
- *                [n,l_k_chunks[c],h_kv,d]  in  bfloat16, device pointers
+ *                [n,l_k_chunks[c],h_kv,d]  in  dtype, device pointers
  *   k_chunks, v_chunks, l_k_chunks, k_offsets: host arrays of n_chunks
  *                entries, read during the call only
- *   out          [n,l_q,h,d]     out  bfloat16
+ *   out          [n,l_q,h,d]     out  dtype
  *   lse          [n,h,l_q]       out  float32, natural log, -inf for rows
  *                with no allowed key in any chunk (O = 0 there)
  *   1 <= n_chunks <= ATTN_RING_MAX_CHUNKS (else ATTN_ERR_SHAPE); a chunk may
  *   have l_k_chunks[c] = 0 (it adds nothing); d in {64, 128}; masking as for
  *   attn_fwd with q_offset and each chunk's k_offsets[c].
  * out and lse must not overlap q or any chunk.  Each chunk is checked as
- * attn_fwd checks k and v.
+ * attn_fwd checks k and v.  ATTN_F32: out and lse themselves serve as the
+ * float32 accumulator, set to the empty result and then merged into by one
+ * fused step (as attn_fwd_acc) per chunk with keys, in the order given:
+ * 1 + (chunks with keys) launches instead of one.
  */
 #define ATTN_RING_MAX_CHUNKS 16
 int attn_fwd_ring(const void* q, const void* const* k_chunks, const void* const* v_chunks,
@@ -323,7 +325,7 @@ int attn_bwd_acc_prepared(const void* dout, const void* q, const void* k, const 
  * the saved global output; flash_sharding.py ring_bwd: dq summed over the
  * chunks and cast to the query dtype).  For the share's query rows q with
  * the forward share's final (out, lse) and the incoming dout:
- *   dq            [n,l_q,h,d]    out  bfloat16: scale * sum over all chunks of
+ *   dq            [n,l_q,h,d]    out  dtype: scale * sum over all chunks of
  *                                     dS K (written, not accumulated)
  *   dk_acc_chunks[c], dv_acc_chunks[c]
  *                 [n,l_k_chunks[c],h_kv,d]  in/out  float32: chunk c's dK and
@@ -336,8 +338,11 @@ int attn_bwd_acc_prepared(const void* dout, const void* q, const void* k, const 
  *   workspace: at least attn_bwd_prepare_bytes(n, l_q, h) bytes of device
  *   scratch (contents on entry do not matter).
  * Equal, up to rounding order, to attn_bwd_acc per chunk with dQ accumulated
- * in float32 and cast at the end.  bf16 only; d in {64, 128}.  No output may
- * overlap an input or another output.
+ * in float32 and cast at the end.  dout, q, out, the chunks and dq all in
+ * dtype; d in {64, 128}.  ATTN_F32: dq itself is the float32 accumulator
+ * (cleared, then D and the base-2 LSE prepared once and one accumulating
+ * backward run per chunk with keys: 2 + 2 x (chunks with keys) launches).
+ * No output may overlap an input or another output.
  */
 int attn_bwd_ring(const void* dout, const void* q, const void* out, const float* lse,
                   const void* const* k_chunks, const void* const* v_chunks,

@@ -147,7 +147,9 @@ def test_fwd_ring_argument_checks():
     assert _fwd_ring([(B, C, 128, 0), (F, F + 4096, -1, 0)]) == ATTN_ERR_SHAPE
     assert _fwd_ring(h=6, h_kv=4) == ATTN_ERR_SHAPE
     assert _fwd_ring(d=96) == ATTN_ERR_UNSUPPORTED
-    assert _fwd_ring(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    # q is 32 KiB in bf16 and 64 KiB in float32: an output 48 KiB past q
+    # overlaps only the float32 one
+    assert _fwd_ring(dtype=ATTN_F32, out=A + 49152) == ATTN_ERR_ALIAS
     assert _fwd_ring(scale=float("nan")) == ATTN_ERR_UNSUPPORTED
     assert _fwd_ring(out=D_ + 8) == ATTN_ERR_ALIGN
     assert _fwd_ring([(B, C, 128, 0), (F + 8, F + 4096, 128, 0)]) == ATTN_ERR_ALIGN
@@ -562,7 +564,9 @@ def test_bwd_ring_checks():
     assert call(l_k=(128, -1)) == ATTN_ERR_SHAPE
     assert call(h=3) == ATTN_ERR_SHAPE
     assert call(d=96) == ATTN_ERR_UNSUPPORTED
-    assert call(dtype=ATTN_F32) == ATTN_ERR_UNSUPPORTED
+    # dout is 32 KiB in bf16 and 64 KiB in float32: a dq 40 KiB past it
+    # overlaps only the float32 one
+    assert call(dtype=ATTN_F32, dq=A + 40960) == ATTN_ERR_ALIAS
     assert call(ws=None) == ATTN_ERR_WORKSPACE
     assert call(wsb=16) == ATTN_ERR_WORKSPACE
     assert call(dka=(F + 8, F + (1 << 30))) == ATTN_ERR_ALIGN

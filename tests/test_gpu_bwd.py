@@ -133,17 +133,19 @@ def test_c5_backward_full():
         check_grad(dv, rv, f"C5 head {g} dv")
 
 
-def test_fp32_one_launch_ring_backward_is_rejected():
-    """The float32 backward runs per step (tests/test_gpu_f32.py); the
-    three-launch ring share is bf16 only and refuses float32 before any
-    launch."""
-    q = torch.zeros((1, 64, 2, 64), device="cuda")
+def test_fp32_one_launch_ring_backward_without_keys():
+    """The float32 three-launch ring share with only empty chunks: dQ = 0 and
+    the accumulators untouched (the float32 forms run on tests/test_gpu_f32.py)."""
+    q = torch.randn((1, 64, 2, 64), device="cuda")
     lse = torch.zeros((1, 2, 64), device="cuda")
-    kc = [torch.zeros((1, 32, 1, 64), device="cuda")]
-    acc = [torch.zeros((1, 32, 1, 64), device="cuda")]
-    with pytest.raises(Exception):
-        A.attn_bwd_ring(q, q, q, lse, kc, kc, [0], acc, [a.clone() for a in acc],
-                        torch.empty_like(q), 0.1, True)
+    kc = [torch.zeros((1, 0, 1, 64), device="cuda")]
+    acc = [torch.ones((1, 0, 1, 64), device="cuda")]
+    dq = torch.full_like(q, float("nan"))
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    A.attn_bwd_ring(q, q, q, lse, kc, kc, [0], acc, [a.clone() for a in acc], dq, 0.1, True,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0)
 
 
 @pytest.mark.parametrize("d,h_kv,window,fused,one_launch", [

@@ -1,8 +1,9 @@
 """GPU parity of the float32 paths against the fp64 oracle, through the C ABI:
 the float32 backward (attn_bwd, attn_bwd_acc, the prepared ring steps,
-attn_bwd_static, the ring backward share) and the float32 fused ring step
-(attn_fwd_acc and the fused ring share).  The GPU backward consumes the GPU
-forward's float32 O and LSE.
+attn_bwd_static, the ring backward share per step and as attn_bwd_ring) and
+the float32 fused ring step (attn_fwd_acc, the fused ring share and
+attn_fwd_ring).  The GPU backward consumes the GPU forward's float32 O and
+LSE.
 
 Tolerance: the pages fix 1e-5 for float32 inputs.  O and LSE: 1e-5
 absolute; gradients: max |g - g_ref| <= 1e-5 * max(1, max |g_ref|), the same
@@ -113,13 +114,18 @@ def test_f32_backward_accumulating_prepared_and_static():
         assert np.array_equal(g, host(s))
 
 
-@pytest.mark.parametrize("d,h_kv,window", [(64, 1, (-1, -1)), (128, 2, (100, 0))])
-def test_f32_ring_share_backward(d, h_kv, window):
+@pytest.mark.parametrize("d,h_kv,window,one", [
+    (64, 1, (-1, -1), False),
+    (128, 2, (100, 0), False),
+    (64, 1, (-1, -1), True),
+    (128, 2, (100, 0), True),
+])
+def test_f32_ring_share_backward(d, h_kv, window, one):
     """Every rank of a ring of P = 3 (chunks of 100, causal), float32: the
-    fused forward share, then the backward share (prepared once, one
-    accumulating step per chunk); dQ against the rank's rows of the
-    full-sequence gradient, each chunk's (dK, dV) against the rank's
-    contribution to that chunk's keys."""
+    forward share (fused steps, or attn_fwd_ring), then the backward share
+    (prepared once, one accumulating step per chunk, or attn_bwd_ring); dQ
+    against the rank's rows of the full-sequence gradient, each chunk's (dK,
+    dV) against the rank's contribution to that chunk's keys."""
     P, c, h = 3, 100, 4
     L = P * c
     q, k, v, do = draw_normal(51 + d, [(1, L, h, d), (1, L, h_kv, d), (1, L, h_kv, d),
@@ -130,16 +136,16 @@ def test_f32_ring_share_backward(d, h_kv, window):
     offs = [s * c for s in range(P)]
     ro, rl = oracle.attention_fwd(q, k, v, scale, True, window[0], window[1])
     for r in range(P):
-        say(f"[f32 ring bwd] d={d} h_kv={h_kv} window={window} rank {r}")
+        say(f"[f32 ring bwd] d={d} h_kv={h_kv} window={window} one launch={one} rank {r}")
         qr, dor = q[:, r * c:(r + 1) * c], do[:, r * c:(r + 1) * c]
         tq, tdo = dev(qr, "f32"), dev(dor, "f32")
-        out, lse = A.ring_share(tq, kc, vc, offs, r * c, scale, True, fused=True,
-                                window=window)
+        out, lse = A.ring_share(tq, kc, vc, offs, r * c, scale, True, fused=not one,
+                                window=window, one_launch=one)
         torch.cuda.synchronize()
         check_o_lse(host(out), host(lse), ro[:, r * c:(r + 1) * c],
                     rl[:, :, r * c:(r + 1) * c], "f32", f"rank {r} fused share")
         share = A.RingShareBwd(tq, out.clone(), lse.clone(), tdo, scale, True, r * c, window)
-        dq, dk_acc, dv_acc = share.run(kc, vc, offs)
+        dq, dk_acc, dv_acc = share.run(kc, vc, offs, one_launch=one)
         torch.cuda.synchronize()
         rq, rk, rv = oracle.attention_bwd(qr, k, v, dor, scale, True, window[0], window[1],
                                           r * c, 0)
@@ -193,3 +199,23 @@ def test_f32_tiny_workload_forward_and_backward():
     check_grad(dq, rq, "dq")
     check_grad(dk, rk, "dk")
     check_grad(dv, rv, "dv")
+
+
+def test_f32_one_launch_share_with_empty_chunk():
+    """attn_fwd_ring in float32 over chunks given out of order, one of them
+    empty, under a window that leaves some rows without any key: equal to
+    attention over the keys of all chunks at their absolute positions."""
+    n, l_q, h, h_kv, d = 1, 90, 4, 2, 64
+    lens, offs = [70, 0, 50], [50, 120, 0]          # keys 50..119, none, 0..49
+    q, k, v = draw_normal(71, [(n, l_q, h, d), (n, 120, h_kv, d), (n, 120, h_kv, d)])
+    scale = 0.11
+    qo, window = 100, (40, 0)                       # rows 60.. see no key
+    kc = [dev(k[:, o:o + m], "f32") for o, m in zip(offs, lens)]
+    vc = [dev(v[:, o:o + m], "f32") for o, m in zip(offs, lens)]
+    tq = dev(q, "f32")
+    out = torch.empty_like(tq)
+    lse = torch.empty((n, h, l_q), dtype=torch.float32, device="cuda")
+    A.attn_fwd_ring(tq, kc, vc, offs, out, lse, scale, True, window[0], window[1], qo)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_fwd(q, k, v, scale, True, window[0], window[1], qo, 0)
+    check_o_lse(host(out), host(lse), ro, rl, "f32", "float32 one-launch share")
