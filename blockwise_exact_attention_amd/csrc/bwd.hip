@@ -578,10 +578,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce(BwdParams p) {
 // over keys, so group 1's partial dQ^T is simply added to group 0's (through
 // LDS) before the epilogue.
 
-template <int D, bool ACC, int KSPLIT, bool MULTI>
-__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq_kernel(
-    BwdParams p, int n_qtiles, int reverse) {
+template <int D, bool ACC, int KSPLIT, bool MULTI, bool WIDE = false>
+__global__ __launch_bounds__(kThreads * (WIDE ? 2 : KSPLIT), KSPLIT == 1 && !WIDE ? 2 : 1)
+    void bwd_dq_kernel(BwdParams p, int n_qtiles, int reverse) {
   static_assert(!MULTI || !ACC, "the multi-chunk form writes dQ");
+  static_assert(!WIDE || (KSPLIT == 1 && !MULTI), "wide: one group of eight waves");
   constexpr int BN = 64;
   constexpr int RB = D * 2;
   constexpr int TB = BN * RB;
@@ -589,7 +590,9 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
   constexpr int NDB = D / 32;
   constexpr int NKB = BN / 32;
   constexpr int NPS = BN / 16;
-  constexpr int BM = 128;
+  // WIDE: eight waves over 256 rows share every K/V tile (half the tile
+  // loads per product of four waves over 128 rows)
+  constexpr int BM = WIDE ? 256 : 128;
   constexpr uint32_t kVC = D == 128 ? 32u : 16u;
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[KSPLIT][TB];
   __shared__ __attribute__((aligned(16))) unsigned char k_lds1[KSPLIT][TB];
@@ -663,10 +666,33 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
   const uint32_t lane_off = tile_lane_offset<D>(wave, lane, kv_row_b);
   uint32_t ka0, va0;
   lds_read_bases<D>(lane, ka0, va0);
+  // this wave's share of the loads of one 64-key tile (WIDE: one of eight
+  // waves, rows (8 x + wave) RPL + lane / CPR of load x)
+  auto dma_tile = [&](const uint16_t* base, long long j0, unsigned char* dst) {
+    if constexpr (!WIDE) {
+      tile_dma<D>(base, j0, (long long)lk_ - j0, kv_row_b, dst, wave, lane_off);
+    } else {
+      constexpr int RPL = 1024 / RB;
+      constexpr int LOADS = BN / RPL / 8;
+      static_assert(LOADS >= 1 && (8 * RPL) % 16 == 0, "wide tile loads");
+      const long long bytes =
+          max(0LL, min(((long long)lk_ - j0) * (long long)kv_row_b, 0x7fffffffLL));
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(base) + (size_t)j0 * (kv_row_b / 2), (short)0, (int)bytes,
+          0x00020000);
+#pragma unroll
+      for (int x = 0; x < LOADS; ++x) {
+        const int row0 = (x * 8 + wave) * RPL;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + row0 * RB), 16,
+                                                 lane_off,
+                                                 (uint32_t)(x * 8 * RPL) * kv_row_b, 0, 0);
+      }
+    }
+  };
   auto load = [&](int kt, unsigned char* kd, unsigned char* vd) {
     const long long j0 = (long long)kt * BN;
-    tile_dma<D>(kbase, j0, (long long)lk_ - j0, kv_row_b, kd, wave, lane_off);
-    tile_dma<D>(vbase, j0, (long long)lk_ - j0, kv_row_b, vd, wave, lane_off);
+    dma_tile(kbase, j0, kd);
+    dma_tile(vbase, j0, vd);
   };
 
   int kt_begin = 0, kt_end = 0;
@@ -817,7 +843,9 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? 2 : 1) void bwd_dq
   uint32_t ln = (uint32_t)lane;
   asm volatile("" : "+v"(ln));
   const uint32_t ecol = ln & 31u, ehalf = ln >> 5;
-  unsigned char* stage = (wave < 2 ? &k_lds0[0][0] : &k_lds1[0][0]) + (wave & 1) * 32 * RB;
+  const int w2 = wave >> 1;   // two waves to each buffer (WIDE: all four)
+  unsigned char* stage = (w2 == 0 ? &k_lds0[0][0] : w2 == 1 ? &k_lds1[0][0]
+                          : w2 == 2 ? &v_lds0[0][0] : &v_lds1[0][0]) + (wave & 1) * 32 * RB;
   static_assert(2 * 32 * RB <= TB, "staging fits");
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -899,15 +927,27 @@ hipError_t launch_bwd_d(const BwdParams& p, int causal, hipStream_t stream, bool
   }
   // dQ: with fewer than two workgroups per CU, each workgroup's key tiles
   // are split over two groups of four waves that add their partial dQ at
-  // the end (two waves per SIMD either way)
+  // the end; at d = 128 with at least one 256-row workgroup per CU, eight
+  // waves share each tile (two waves per SIMD in every form; at d = 64 the
+  // four-wave form runs three per SIMD)
   const int n_qtiles = (p.l_q + 127) / 128;
   const long long dq_wgs = (long long)n_qtiles * p.n * p.h;
-  if (dq_wgs < 2 * kDqCUs)
+  const int n_wide = (p.l_q + 255) / 256;
+  const long long wide_wgs = (long long)n_wide * p.n * p.h;
+  if (dq_wgs < 2 * kDqCUs) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 2, false>), dim3((unsigned)dq_wgs), dim3(2 * kThreads),
                        0, stream, p, n_qtiles, causal ? 1 : 0);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 1, false>), dim3((unsigned)dq_wgs), dim3(kThreads),
-                       0, stream, p, n_qtiles, causal ? 1 : 0);
+    return hipGetLastError();
+  }
+  if constexpr (D == 128) {
+    if (wide_wgs >= kDqCUs) {
+      hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 1, false, true>), dim3((unsigned)wide_wgs),
+                         dim3(2 * kThreads), 0, stream, p, n_wide, causal ? 1 : 0);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<D, ACC, 1, false>), dim3((unsigned)dq_wgs), dim3(kThreads),
+                     0, stream, p, n_qtiles, causal ? 1 : 0);
   return hipGetLastError();
 }
 
