@@ -577,6 +577,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce(BwdParams p) {
 // group with its own LDS buffers and alternate key tiles; dQ is a plain sum
 // over keys, so group 1's partial dQ^T is simply added to group 0's (through
 // LDS) before the epilogue.
+//
+// WIDE: eight waves over 256 rows, one group: every K/V tile loaded once
+// for twice the rows.
 
 template <int D, bool ACC, int KSPLIT, bool MULTI, bool WIDE = false>
 __global__ __launch_bounds__(kThreads * (WIDE ? 2 : KSPLIT), KSPLIT == 1 && !WIDE ? 2 : 1)
