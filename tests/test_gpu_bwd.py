@@ -115,6 +115,25 @@ def test_backward_is_deterministic():
         assert torch.equal(x, y)
 
 
+def test_wide_dq_ragged_grouped():
+    """A backward whose dQ runs the wide form (eight waves over 256 query
+    rows, d = 128, at least one 256-row workgroup per CU): ragged length
+    (2200 = 8 x 256 + 152), grouped heads 32/8, causal with a query offset;
+    three whole key/value groups (their 12 query heads) against the oracle."""
+    n, l_q, l_k, h, h_kv, d = 1, 2200, 2300, 32, 8, 128
+    q, k, v, do = draw_normal(17, [(n, l_q, h, d), (n, l_k, h_kv, d), (n, l_k, h_kv, d),
+                                   (n, l_q, h, d)])
+    q, k, v, do = (round_to_bf16(x) for x in (q, k, v, do))
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = run_fwd_bwd(q, k, v, do, scale, True, qo=100)
+    for g in (0, 5, 7):
+        rq, rk, rv = oracle.attention_bwd(q, k, v, do, scale, True, -1, -1, 100, 0,
+                                          kv_heads=[(0, g)], block=1024)
+        check_grad(dq, rq, f"group {g} dq")
+        check_grad(dk, rk, f"group {g} dk")
+        check_grad(dv, rv, f"group {g} dv")
+
+
 def test_c5_backward_full():
     """Long-context workload at full size (l = 16384, 16 heads): every
     gradient of every head against the oracle (head by head, about three
