@@ -57,6 +57,18 @@ def test_c2_causal_mha_full():
     check_o_lse(o, lse, ro, rl, "bf16", "C2")
 
 
+def test_mqa_at_the_c2_shape_full():
+    """The multi-query variant the benchmark also times (2 x 2048 tokens, 16
+    query heads reading one key/value head, d = 128, causal): every head and
+    row against the oracle."""
+    q, k, v = (round_to_bf16(x) for x in draw_normal(
+        203, [(2, 2048, 16, 128), (2, 2048, 1, 128), (2, 2048, 1, 128)]))
+    scale = 1.0 / math.sqrt(128)
+    o, lse = run_fwd(q, k, v, "bf16", scale, True)
+    ro, rl = oracle.attention_fwd(q, k, v, scale, True)
+    check_o_lse(o, lse, ro, rl, "bf16", "MQA at the C2 shape")
+
+
 def test_c3_ring_share():
     """Rank 7 of 8: the merged share equals rows 7168..8191 of causal
     attention over the full 8192-token sequence, on every head and row."""
